@@ -1,0 +1,13 @@
+"""fp64 CPU oracle for exact shared-prefix attention (test infrastructure).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline`` leg may
+import anything under ``oracle/``. The GPU library (``shared_prefix_attention_prompt_amd``)
+never does, and the two share no code: only the seeded input generator in ``workloads``
+feeds both.
+
+Every function here is pinned by the ``-m "not gpu"`` tests in ``tests/test_oracle_*.py``
+(hand-derived golden values, closed forms, a library attention routine under an explicit
+tree mask, finite differences, and invariants of the mathematics).
+"""
+from .flat_attention import (rows_attention, flattened_tree_attention,  # noqa: F401
+                             flattened_sampled_rows, branch_response_grads)
