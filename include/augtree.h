@@ -1,0 +1,147 @@
+/*
+ * augtree.h -- C ABI of exact shared-prefix attention on MI355X (gfx950).
+ *
+ * One attention layer over a replay tree: one prompt of P tokens shared by G response
+ * branches ("Splitting Prompt Prefill from Response Replay for Context-Parallel
+ * Long-Context LLM Post-Training", Bao et al., §2.1 replay tree; §3.2 Eq. 1 dependency).
+ * A prompt token attends causally to the prompt; a token of branch i attends to the whole
+ * prompt and causally to branch i, never to a sibling. The prompt is evaluated once
+ * (prefill, §3.2); the branches are evaluated against the stationary prompt K/V plus
+ * their own K/V (replay, §3.3 MoveQ), and the two partial softmax states are merged
+ * exactly (§3.3, Fig. 8). Backward sums every branch's prompt K/V gradient into one
+ * prompt gradient (§3.2, equation after Eq. 1) and then adds the prompt queries' own
+ * contribution, as the accumulated prompt gradient flows back through the prefill graph.
+ *
+ * Call order for one layer (§3.2): augtree_prefill_fwd -> augtree_replay_fwd ->
+ * augtree_replay_bwd -> augtree_prefill_bwd.
+ *
+ * Data layout (all device buffers, row-major, contiguous, no strides):
+ *   prompt   q_p, o_p, do_p, dq_p          [P][Hq][D]     (dtype)
+ *            k_p, v_p, dk_p, dv_p          [P][Hkv][D]    (dtype)
+ *   response q_r, o_r, do_r, dq_r          [T_R][Hq][D]   (dtype), branches packed back to back
+ *            k_r, v_r, dk_r, dv_r          [T_R][Hkv][D]  (dtype)
+ *   lse_p [Hq][P], lse_r [Hq][T_R]         float32, natural log of sum_j exp(scale*q.k_j)
+ *   dk_p_acc, dv_p_acc [P][Hkv][D]         float32, branches' summed prompt K/V gradient
+ * where T_R = branch_offsets[G] and query head h reads key/value head h / (Hq/Hkv).
+ * dtype is float32 or bfloat16; accumulation is always float32 and each bf16 output is
+ * rounded once, to nearest even. Every device pointer must be 16-byte aligned.
+ *
+ * Ownership: the caller allocates every buffer, the workspace included (size from
+ * augtree_workspace_bytes). The library allocates, frees and synchronises nothing, keeps
+ * no pointer after a call returns, and enqueues all work on `stream` (a hipStream_t; NULL
+ * is the null stream). Buffers must stay alive until that work completes.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued. On an error
+ * the call returns a non-zero status and enqueues nothing, except AUGTREE_ERR_HIP, which
+ * may follow a partial enqueue. augtree_last_error() then describes the failure (per
+ * thread). No C++ exception crosses this interface. The library holds no mutable global
+ * state and may be called from several host threads.
+ *
+ * Results are bitwise reproducible for identical inputs and dims: no floating-point
+ * atomics are used anywhere; every reduction runs in a fixed order.
+ */
+#ifndef AUGTREE_H
+#define AUGTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AUGTREE_ABI_VERSION 1
+#define AUGTREE_MAX_BRANCHES 128
+
+typedef enum { AUGTREE_F32 = 0, AUGTREE_BF16 = 1 } augtree_dtype;
+
+typedef enum {
+  AUGTREE_OK = 0,
+  AUGTREE_ERR_INVALID_ARGUMENT = 1, /* bad size, offsets, pointer or alignment */
+  AUGTREE_ERR_UNSUPPORTED = 2,      /* valid but not built: head_dim other than 64/128 */
+  AUGTREE_ERR_WORKSPACE = 3,        /* workspace NULL or smaller than required */
+  AUGTREE_ERR_HIP = 4               /* a HIP launch or runtime call failed */
+} augtree_status;
+
+/* Operation codes for augtree_workspace_bytes. */
+enum { AUGTREE_OP_PREFILL_FWD = 0, AUGTREE_OP_REPLAY_FWD = 1, AUGTREE_OP_REPLAY_BWD = 2,
+       AUGTREE_OP_PREFILL_BWD = 3 };
+
+/* Sizes of one replay tree. Only branch_offsets is a HOST pointer. */
+typedef struct {
+  int32_t prompt_len;             /* P >= 1 */
+  int32_t num_branches;           /* 1 <= G <= AUGTREE_MAX_BRANCHES */
+  const int32_t *branch_offsets;  /* host, G+1 entries: [0] = 0, strictly increasing (every
+                                     branch has >= 1 token), [G] = T_R; branch i is packed
+                                     rows [offsets[i], offsets[i+1]) */
+  int32_t num_q_heads;            /* Hq >= 1 */
+  int32_t num_kv_heads;           /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;               /* D: 64 or 128 */
+  float softmax_scale;            /* > 0 and finite; attention uses softmax(scale*QK^T) */
+  int32_t dtype;                  /* augtree_dtype of Q, K, V, O, dO and every gradient */
+} augtree_dims;
+
+/* Causal attention of the prompt over itself, computed once for all branches (§3.2,
+ * shared prompt prefill; attention definition §2.2).
+ * in:  q_p [P][Hq][D], k_p/v_p [P][Hkv][D]   out: o_p [P][Hq][D], lse_p [Hq][P].
+ * Workspace: augtree_workspace_bytes(dims, AUGTREE_OP_PREFILL_FWD) (0: ws may be NULL). */
+augtree_status augtree_prefill_fwd(const augtree_dims *dims, const void *q_p, const void *k_p,
+                                   const void *v_p, void *o_p, float *lse_p, void *ws,
+                                   size_t ws_bytes, void *stream);
+
+/* Response replay against the stationary prompt K/V (§3.3 MoveQ; §3.2 response replay
+ * with the cached prompt state): every branch row attends to all P prompt keys (one dense
+ * partial state per row), then causally to its own branch (a second partial state); the
+ * two states are merged by the log-sum-exp rule of §3.3 (Fig. 8).
+ * in:  k_p/v_p [P][Hkv][D], q_r [T_R][Hq][D], k_r/v_r [T_R][Hkv][D]
+ * out: o_r [T_R][Hq][D], lse_r [Hq][T_R].
+ * Workspace: the two partial states (2 * T_R*Hq*(D+1) floats). */
+augtree_status augtree_replay_fwd(const augtree_dims *dims, const void *k_p, const void *v_p,
+                                  const void *q_r, const void *k_r, const void *v_r, void *o_r,
+                                  float *lse_r, void *ws, size_t ws_bytes, void *stream);
+
+/* Backward of augtree_replay_fwd for the loss sum(o_r * do_r) (§3.3: gradients return to
+ * the query and K/V owners; §3.2: prompt K/V gradient summed over branches).
+ * in:  k_p, v_p, q_r, k_r, v_r, o_r, lse_r (as produced by augtree_replay_fwd), do_r
+ * out: dq_r [T_R][Hq][D], dk_r/dv_r [T_R][Hkv][D] (own-branch contributions; complete),
+ *      dk_p_acc/dv_p_acc [P][Hkv][D] float32: the sum over all branches and all query
+ *      heads of each group of the prompt K/V gradient (overwritten, not accumulated into).
+ * Workspace: row statistics and, for long prompts, split partial sums. */
+augtree_status augtree_replay_bwd(const augtree_dims *dims, const void *k_p, const void *v_p,
+                                  const void *q_r, const void *k_r, const void *v_r,
+                                  const void *o_r, const float *lse_r, const void *do_r,
+                                  void *dq_r, void *dk_r, void *dv_r, float *dk_p_acc,
+                                  float *dv_p_acc, void *ws, size_t ws_bytes, void *stream);
+
+/* Backward of augtree_prefill_fwd for the loss sum(o_p * do_p), with the branches'
+ * prompt K/V gradient added in (§3.2: accumulated prompt gradients flow back through the
+ * prefill graph).
+ * in:  q_p, k_p, v_p, o_p, lse_p (as produced by augtree_prefill_fwd), do_p,
+ *      dk_p_acc/dv_p_acc from augtree_replay_bwd, or both NULL (no branches: plain causal
+ *      attention backward)
+ * out: dq_p [P][Hq][D], dk_p/dv_p [P][Hkv][D] = prompt queries' contribution + acc,
+ *      rounded once to dtype.
+ * Workspace: row statistics (Hq*P floats). */
+augtree_status augtree_prefill_bwd(const augtree_dims *dims, const void *q_p, const void *k_p,
+                                   const void *v_p, const void *o_p, const float *lse_p,
+                                   const void *do_p, const float *dk_p_acc,
+                                   const float *dv_p_acc, void *dq_p, void *dk_p, void *dv_p,
+                                   void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of workspace operation `op` (AUGTREE_OP_*) needs for `dims`; 0 for invalid dims. */
+size_t augtree_workspace_bytes(const augtree_dims *dims, int op);
+
+/* Static text of a status code. */
+const char *augtree_status_string(augtree_status status);
+
+/* Detail of the last failed call on the calling thread ("" if none). */
+const char *augtree_last_error(void);
+
+/* AUGTREE_ABI_VERSION of the built library. */
+int augtree_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AUGTREE_H */

@@ -209,8 +209,6 @@ def flattened_sampled_rows(q_p, k_p, v_p, q_r, k_r, v_r, offsets, prompt_rows: S
     Returns o_p [n_p][Hq][D], lse_p [Hq][n_p], o_r [n_r][Hq][D], lse_r [Hq][n_r] and, with
     backward, dq_p [n_p][Hq][D], dq_r [n_r][Hq][D].
     """
-    q_p, k_p, v_p = _as64(q_p), _as64(k_p), _as64(v_p)
-    q_r, k_r, v_r = _as64(q_r), _as64(k_r), _as64(v_r)
     off = [int(x) for x in (offsets.tolist() if torch.is_tensor(offsets) else offsets)]
     P, Hq, D = q_p.shape
     Hkv = k_p.shape[1]
@@ -220,7 +218,6 @@ def flattened_sampled_rows(q_p, k_p, v_p, q_r, k_r, v_r, offsets, prompt_rows: S
         scale = 1.0 / D ** 0.5
     backward = do_p is not None
     if backward:
-        do_p, do_r = _as64(do_p), _as64(do_r)
         w = [1.0 / G] * G if prompt_grad_weights is None else [float(x) for x in prompt_grad_weights]
     prows = torch.tensor(sorted(set(int(r) for r in prompt_rows)), dtype=torch.long)
     rrows = torch.tensor(sorted(set(int(r) for r in response_rows)), dtype=torch.long)
@@ -234,16 +231,20 @@ def flattened_sampled_rows(q_p, k_p, v_p, q_r, k_r, v_r, offsets, prompt_rows: S
 
     for h in range(Hq):
         g = h // group
+        # per-head fp64 slices (inputs may be large; only one head is held in fp64)
+        kp_g, vp_g = _as64(k_p[:, g]), _as64(v_p[:, g])
+        kr_g, vr_g = _as64(k_r[:, g]), _as64(v_r[:, g])
         # prompt rows: evaluated in every flattened copy (each copy's prefix is the prompt)
         if np_:
             last = int(prows.max()) + 1
             for i in range(G):
-                k = _branch_seq(k_p[:, g], k_r[:, g], off, i)[:last]
-                v = _branch_seq(v_p[:, g], v_r[:, g], off, i)[:last]
-                q = q_p[prows, h]
+                k = _branch_seq(kp_g, kr_g, off, i)[:last]
+                v = _branch_seq(vp_g, vr_g, off, i)[:last]
+                q = _as64(q_p[prows, h])
                 counts = prows + 1
                 if backward:
-                    o, lse, dq, _, _ = rows_attention(q, k, v, counts, scale, do_p[prows, h] * w[i])
+                    o, lse, dq, _, _ = rows_attention(q, k, v, counts, scale,
+                                                      _as64(do_p[prows, h]) * w[i])
                     out["dq_p"][:, h] += dq
                 else:
                     o, lse = rows_attention(q, k, v, counts, scale)
@@ -256,13 +257,14 @@ def flattened_sampled_rows(q_p, k_p, v_p, q_r, k_r, v_r, offsets, prompt_rows: S
             if len(sel) == 0:
                 continue
             rows = rrows[sel]
-            k = _branch_seq(k_p[:, g], k_r[:, g], off, i)
-            v = _branch_seq(v_p[:, g], v_r[:, g], off, i)
+            k = _branch_seq(kp_g, kr_g, off, i)
+            v = _branch_seq(vp_g, vr_g, off, i)
             counts = P + (rows - off[i]) + 1
             last = int(counts.max())
-            q = q_r[rows, h]
+            q = _as64(q_r[rows, h])
             if backward:
-                o, lse, dq, _, _ = rows_attention(q, k[:last], v[:last], counts, scale, do_r[rows, h])
+                o, lse, dq, _, _ = rows_attention(q, k[:last], v[:last], counts, scale,
+                                                  _as64(do_r[rows, h]))
                 out["dq_r"][sel, h] = dq
             else:
                 o, lse = rows_attention(q, k[:last], v[:last], counts, scale)
@@ -281,8 +283,6 @@ def branch_response_grads(q_p, k_p, v_p, q_r, k_r, v_r, offsets, branch: int, do
     normalised over its whole flattened sequence). Returns dk_r, dv_r [R_i][h][D] for the
     selected kv heads, plus dq_r, o_r, lse_r of those rows for the group's query heads.
     """
-    q_p, k_p, v_p = _as64(q_p), _as64(k_p), _as64(v_p)
-    q_r, k_r, v_r, do_r = _as64(q_r), _as64(k_r), _as64(v_r), _as64(do_r)
     off = [int(x) for x in (offsets.tolist() if torch.is_tensor(offsets) else offsets)]
     P, Hq, D = q_p.shape
     Hkv = k_p.shape[1]
@@ -301,10 +301,10 @@ def branch_response_grads(q_p, k_p, v_p, q_r, k_r, v_r, offsets, branch: int, do
     for a, h in enumerate(qhs):
         g = h // group
         b = kvs.index(g)
-        k = _branch_seq(k_p[:, g], k_r[:, g], off, i)
-        v = _branch_seq(v_p[:, g], v_r[:, g], off, i)
-        q = q_r[off[i]:off[i + 1], h]
-        do = do_r[off[i]:off[i + 1], h]
+        k = _branch_seq(_as64(k_p[:, g]), _as64(k_r[:, g]), off, i)
+        v = _branch_seq(_as64(v_p[:, g]), _as64(v_r[:, g]), off, i)
+        q = _as64(q_r[off[i]:off[i + 1], h])
+        do = _as64(do_r[off[i]:off[i + 1], h])
         for r0 in range(0, R, slab):
             r1 = min(R, r0 + slab)
             counts = P + torch.arange(r0, r1) + 1

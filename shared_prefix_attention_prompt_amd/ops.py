@@ -1,0 +1,164 @@
+"""Torch-facing wrappers of the four C-ABI entry points, and the autograd function.
+
+PyTorch provides device memory and the current HIP stream; every step of the attention
+runs in the HIP kernels of libaugtree.so. Tensors must be contiguous, on one GPU, in
+float32 or bfloat16, with the layouts of include/augtree.h.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.AUGTREE_F32, torch.bfloat16: _lib.AUGTREE_BF16}
+
+
+def _offsets_list(offsets) -> list:
+    if torch.is_tensor(offsets):
+        return [int(x) for x in offsets.detach().to("cpu").tolist()]
+    return [int(x) for x in offsets]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_tensors(*named):
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    return dev
+
+
+def _dims(P, offsets, Hq, Hkv, D, scale, dtype):
+    if dtype not in _DT:
+        raise ValueError(f"unsupported dtype {dtype}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return _lib.make_dims(P, offsets, Hq, Hkv, D, scale, _DT[dtype])
+
+
+def _workspace(dims, op, device):
+    n = _lib.workspace_bytes(dims, op)
+    if n == 0:
+        return None, 0
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def prefill_fwd(q_p, k_p, v_p, scale: Optional[float] = None, offsets: Sequence[int] = (0, 1)
+                ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Causal prompt attention: (o_p [P][Hq][D], lse_p [Hq][P] float32)."""
+    dev = _check_tensors(("q_p", q_p), ("k_p", k_p), ("v_p", v_p))
+    P, Hq, D = q_p.shape
+    dims, keep = _dims(P, _offsets_list(offsets), Hq, k_p.shape[1], D, scale, q_p.dtype)
+    o_p = torch.empty_like(q_p)
+    lse_p = torch.empty(Hq, P, dtype=torch.float32, device=dev)
+    ws, n = _workspace(dims, _lib.AUGTREE_OP_PREFILL_FWD, dev)
+    st = _lib.augtree_prefill_fwd(dims, q_p.data_ptr(), k_p.data_ptr(), v_p.data_ptr(), o_p.data_ptr(),
+                                  lse_p.data_ptr(), _ptr(ws), n, _stream(dev))
+    _lib._check(st, "augtree_prefill_fwd")
+    return o_p, lse_p
+
+
+def replay_fwd(k_p, v_p, q_r, k_r, v_r, offsets, scale: Optional[float] = None
+               ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Branch rows against the stationary prompt K/V and their own branch:
+    (o_r [T][Hq][D], lse_r [Hq][T] float32)."""
+    dev = _check_tensors(("k_p", k_p), ("v_p", v_p), ("q_r", q_r), ("k_r", k_r), ("v_r", v_r))
+    T, Hq, D = q_r.shape
+    dims, keep = _dims(k_p.shape[0], _offsets_list(offsets), Hq, k_p.shape[1], D, scale, q_r.dtype)
+    o_r = torch.empty_like(q_r)
+    lse_r = torch.empty(Hq, T, dtype=torch.float32, device=dev)
+    ws, n = _workspace(dims, _lib.AUGTREE_OP_REPLAY_FWD, dev)
+    st = _lib.augtree_replay_fwd(dims, k_p.data_ptr(), v_p.data_ptr(), q_r.data_ptr(), k_r.data_ptr(),
+                                 v_r.data_ptr(), o_r.data_ptr(), lse_r.data_ptr(), _ptr(ws), n, _stream(dev))
+    _lib._check(st, "augtree_replay_fwd")
+    return o_r, lse_r
+
+
+def replay_bwd(k_p, v_p, q_r, k_r, v_r, offsets, o_r, lse_r, do_r, scale: Optional[float] = None):
+    """(dq_r, dk_r, dv_r, dk_p_acc, dv_p_acc): branch gradients and the branches' summed
+    prompt K/V gradient in float32."""
+    dev = _check_tensors(("k_p", k_p), ("v_p", v_p), ("q_r", q_r), ("k_r", k_r), ("v_r", v_r),
+                         ("o_r", o_r), ("lse_r", lse_r), ("do_r", do_r))
+    T, Hq, D = q_r.shape
+    P, Hkv = k_p.shape[0], k_p.shape[1]
+    dims, keep = _dims(P, _offsets_list(offsets), Hq, Hkv, D, scale, q_r.dtype)
+    dq_r = torch.empty_like(q_r)
+    dk_r = torch.empty_like(k_r)
+    dv_r = torch.empty_like(v_r)
+    dk_acc = torch.empty(P, Hkv, D, dtype=torch.float32, device=dev)
+    dv_acc = torch.empty(P, Hkv, D, dtype=torch.float32, device=dev)
+    ws, n = _workspace(dims, _lib.AUGTREE_OP_REPLAY_BWD, dev)
+    st = _lib.augtree_replay_bwd(dims, k_p.data_ptr(), v_p.data_ptr(), q_r.data_ptr(), k_r.data_ptr(),
+                                 v_r.data_ptr(), o_r.data_ptr(), lse_r.data_ptr(), do_r.data_ptr(),
+                                 dq_r.data_ptr(), dk_r.data_ptr(), dv_r.data_ptr(), dk_acc.data_ptr(),
+                                 dv_acc.data_ptr(), _ptr(ws), n, _stream(dev))
+    _lib._check(st, "augtree_replay_bwd")
+    return dq_r, dk_r, dv_r, dk_acc, dv_acc
+
+
+def prefill_bwd(q_p, k_p, v_p, o_p, lse_p, do_p, dk_p_acc=None, dv_p_acc=None,
+                scale: Optional[float] = None, offsets: Sequence[int] = (0, 1)):
+    """(dq_p, dk_p, dv_p): prompt gradients including the branches' accumulated prompt
+    K/V gradient when given."""
+    dev = _check_tensors(("q_p", q_p), ("k_p", k_p), ("v_p", v_p), ("o_p", o_p), ("lse_p", lse_p),
+                         ("do_p", do_p), ("dk_p_acc", dk_p_acc), ("dv_p_acc", dv_p_acc))
+    P, Hq, D = q_p.shape
+    dims, keep = _dims(P, _offsets_list(offsets), Hq, k_p.shape[1], D, scale, q_p.dtype)
+    dq_p = torch.empty_like(q_p)
+    dk_p = torch.empty_like(k_p)
+    dv_p = torch.empty_like(v_p)
+    ws, n = _workspace(dims, _lib.AUGTREE_OP_PREFILL_BWD, dev)
+    st = _lib.augtree_prefill_bwd(dims, q_p.data_ptr(), k_p.data_ptr(), v_p.data_ptr(), o_p.data_ptr(),
+                                  lse_p.data_ptr(), do_p.data_ptr(), _ptr(dk_p_acc), _ptr(dv_p_acc),
+                                  dq_p.data_ptr(), dk_p.data_ptr(), dv_p.data_ptr(), _ptr(ws), n,
+                                  _stream(dev))
+    _lib._check(st, "augtree_prefill_bwd")
+    return dq_p, dk_p, dv_p
+
+
+class SharedPrefixAttention(torch.autograd.Function):
+    """Drop-in attention over a replay tree: prefill once, replay all branches, and in
+    backward sum every branch's prompt K/V gradient into the prompt gradient."""
+
+    @staticmethod
+    def forward(ctx, q_p, k_p, v_p, q_r, k_r, v_r, offsets, scale):
+        off = _offsets_list(offsets)
+        o_p, lse_p = prefill_fwd(q_p, k_p, v_p, scale, off)
+        o_r, lse_r = replay_fwd(k_p, v_p, q_r, k_r, v_r, off, scale)
+        ctx.save_for_backward(q_p, k_p, v_p, q_r, k_r, v_r, o_p, lse_p, o_r, lse_r)
+        ctx.off = off
+        ctx.scale = scale
+        return o_p, o_r
+
+    @staticmethod
+    def backward(ctx, do_p, do_r):
+        q_p, k_p, v_p, q_r, k_r, v_r, o_p, lse_p, o_r, lse_r = ctx.saved_tensors
+        do_p = torch.zeros_like(o_p) if do_p is None else do_p.contiguous()
+        do_r = torch.zeros_like(o_r) if do_r is None else do_r.contiguous()
+        dq_r, dk_r, dv_r, dk_acc, dv_acc = replay_bwd(k_p, v_p, q_r, k_r, v_r, ctx.off, o_r, lse_r,
+                                                      do_r, ctx.scale)
+        dq_p, dk_p, dv_p = prefill_bwd(q_p, k_p, v_p, o_p, lse_p, do_p, dk_acc, dv_acc, ctx.scale, ctx.off)
+        return dq_p, dk_p, dv_p, dq_r, dk_r, dv_r, None, None
+
+
+def shared_prefix_attention(q_p, k_p, v_p, q_r, k_r, v_r, offsets, scale: Optional[float] = None):
+    """(o_p, o_r) with autograd support; see :class:`SharedPrefixAttention`."""
+    return SharedPrefixAttention.apply(q_p, k_p, v_p, q_r, k_r, v_r, offsets, scale)

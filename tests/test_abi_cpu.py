@@ -1,0 +1,129 @@
+"""The C-ABI library loads, exports every function include/augtree.h declares, and rejects
+bad arguments on the host before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from shared_prefix_attention_prompt_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "augtree.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libaugtree.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(augtree_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_bound_entry_points():
+    assert declared_functions() == sorted(_lib.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True)
+    if out.returncode == 0:
+        exported = set(re.findall(r"\bT (augtree_\w+)", out.stdout))
+        assert set(declared_functions()) <= exported
+
+
+def test_version_and_status_strings():
+    assert _lib.abi_version() == 1
+    assert _lib.status_string(_lib.AUGTREE_OK) == "AUGTREE_OK"
+    assert _lib.status_string(_lib.AUGTREE_ERR_WORKSPACE) == "AUGTREE_ERR_WORKSPACE"
+    assert _lib.status_string(99) == "AUGTREE_ERR_UNKNOWN"
+
+
+def _dims(P=16, off=(0, 4, 9), Hq=4, Hkv=2, D=128, scale=0.088, dtype=_lib.AUGTREE_BF16):
+    return _lib.make_dims(P, list(off), Hq, Hkv, D, scale, dtype)
+
+
+def test_workspace_sizes():
+    d, keep = _dims(P=100, off=(0, 30, 70), Hq=4, Hkv=2, D=128)
+    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_PREFILL_FWD) == 0
+    T, Hq, D = 70, 4, 128
+    rf = _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_FWD)
+    assert rf >= 2 * T * Hq * D * 4 + 2 * T * Hq * 4
+    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_BWD) >= T * Hq * 4
+    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_PREFILL_BWD) >= 100 * Hq * 4
+    assert _lib.workspace_bytes(d, 7) == 0
+    bad, keep2 = _dims(off=(0, 4, 4))
+    assert _lib.workspace_bytes(bad, _lib.AUGTREE_OP_REPLAY_FWD) == 0
+
+
+FAKE = 1 << 20  # 16-byte aligned, never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(P=0), _lib.AUGTREE_ERR_INVALID_ARGUMENT, "prompt_len"),
+    (dict(off=(1, 4)), _lib.AUGTREE_ERR_INVALID_ARGUMENT, "branch_offsets[0]"),
+    (dict(off=(0, 4, 4)), _lib.AUGTREE_ERR_INVALID_ARGUMENT, "strictly increasing"),
+    (dict(off=(0, 5, 3)), _lib.AUGTREE_ERR_INVALID_ARGUMENT, "strictly increasing"),
+    (dict(Hq=3, Hkv=2), _lib.AUGTREE_ERR_INVALID_ARGUMENT, "multiple"),
+    (dict(Hkv=0), _lib.AUGTREE_ERR_INVALID_ARGUMENT, "head counts"),
+    (dict(D=96), _lib.AUGTREE_ERR_UNSUPPORTED, "head_dim"),
+    (dict(D=128, dtype=_lib.AUGTREE_F32), _lib.AUGTREE_ERR_UNSUPPORTED, "head_dim"),
+    (dict(D=0), _lib.AUGTREE_ERR_INVALID_ARGUMENT, "head_dim"),
+    (dict(scale=0.0), _lib.AUGTREE_ERR_INVALID_ARGUMENT, "softmax_scale"),
+    (dict(scale=float("inf")), _lib.AUGTREE_ERR_INVALID_ARGUMENT, "softmax_scale"),
+    (dict(dtype=5), _lib.AUGTREE_ERR_INVALID_ARGUMENT, "dtype"),
+])
+def test_invalid_dims_are_rejected(kw, status, needle):
+    d, keep = _dims(**kw)
+    st = _lib.augtree_prefill_fwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == status
+    assert needle in _lib.last_error()
+
+
+def test_too_many_branches_rejected():
+    off = list(range(0, 130))
+    d, keep = _lib.make_dims(8, off, 2, 2, 128, 0.1, _lib.AUGTREE_BF16)
+    assert d.num_branches == 129
+    st = _lib.augtree_replay_fwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == _lib.AUGTREE_ERR_INVALID_ARGUMENT and "num_branches" in _lib.last_error()
+
+
+def test_null_and_misaligned_pointers_rejected():
+    d, keep = _dims()
+    st = _lib.augtree_prefill_fwd(d, None, FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == _lib.AUGTREE_ERR_INVALID_ARGUMENT and "q_p is NULL" in _lib.last_error()
+    st = _lib.augtree_prefill_fwd(d, FAKE, FAKE + 2, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == _lib.AUGTREE_ERR_INVALID_ARGUMENT and "k_p is not 16-byte aligned" in _lib.last_error()
+    st = _lib.augtree_prefill_bwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                  FAKE, 1 << 30, None)
+    assert st == _lib.AUGTREE_ERR_INVALID_ARGUMENT and "both" in _lib.last_error()
+
+
+def test_missing_or_small_workspace_rejected():
+    d, keep = _dims()
+    need = _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_FWD)
+    st = _lib.augtree_replay_fwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None)
+    assert st == _lib.AUGTREE_ERR_WORKSPACE
+    st = _lib.augtree_replay_fwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None)
+    assert st == _lib.AUGTREE_ERR_WORKSPACE and "needed" in _lib.last_error()
+    st = _lib.augtree_replay_fwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, need, None)
+    assert st == _lib.AUGTREE_ERR_WORKSPACE and "aligned" in _lib.last_error()
+    need_b = _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_BWD)
+    st = _lib.augtree_replay_bwd(d, *([FAKE] * 13), None, need_b, None)
+    assert st == _lib.AUGTREE_ERR_WORKSPACE
+
+
+def test_last_error_is_per_thread():
+    import threading
+    d, keep = _dims(P=0)
+    _lib.augtree_prefill_fwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    main_msg = _lib.last_error()
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(_lib.last_error()))
+    t.start()
+    t.join()
+    assert "prompt_len" in main_msg and seen == [""]

@@ -1,0 +1,166 @@
+"""GPU parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances: fp32 inputs max abs 1e-4; bf16 inputs (fp32 accumulation) max abs 2e-2 and
+relative L2 1e-2, on every output, LSE and gradient. Workloads too large for the full
+flattened oracle are checked on one full key/value group, on sampled rows (a row's O, LSE
+and dQ depend only on its own flattened sequence), on one branch's own K/V gradients, and
+on sum rules that hold at any size.
+"""
+import random
+
+import pytest
+import torch
+
+from oracle import branch_response_grads, flattened_sampled_rows, flattened_tree_attention
+from tests.gpu_run import compare, config_inputs, log, run_path, sum_rules, upload
+from workloads import make_inputs, make_shape
+
+pytestmark = pytest.mark.gpu
+
+ALL = ["o_p", "lse_p", "o_r", "lse_r", "dq_p", "dk_p", "dv_p", "dq_r", "dk_r", "dv_r"]
+
+
+def _full_check(w, keys, kv_heads=None):
+    log(f"case P={w.shape.P} lens={list(w.shape.lens)[:8]} Hq={w.shape.Hq} Hkv={w.shape.Hkv} "
+        f"D={w.shape.D} {w.shape.dtype}")
+    out = run_path(w, backward=w.shape.backward)
+    ref = flattened_tree_attention(w.q_p, w.k_p, w.v_p, w.q_r, w.k_r, w.v_r, w.offsets,
+                                   do_p=w.do_p, do_r=w.do_r, kv_heads=kv_heads)
+    qh = ref["q_heads"].tolist()
+    kh = ref["kv_heads"].tolist()
+    report = []
+    for k in keys:
+        g = out[k]
+        if k.startswith("lse"):
+            g = g[qh]
+        elif k in ("dk_p", "dv_p", "dk_r", "dv_r"):
+            g = g[:, kh]
+        else:
+            g = g[:, qh]
+        compare(k, g, ref[k], w.shape.dtype, report)
+    log("  " + ", ".join(f"{n} {e:.1e}/{r:.1e}" for n, e, r, _ in report))
+    return out
+
+
+def test_config1_fp32_full():
+    w = config_inputs(1)
+    _full_check(w, ALL)
+
+
+@pytest.mark.parametrize("P,lens,Hq,Hkv,D,dtype", [
+    (1, [1], 1, 1, 64, "f32"),
+    (70, [3, 100, 1], 2, 1, 64, "f32"),
+    (1, [1], 1, 1, 128, "bf16"),
+    (5, [1, 2, 3], 2, 2, 64, "bf16"),
+    (130, [1, 63, 64, 65, 129], 4, 2, 128, "bf16"),
+    (257, [200, 5], 8, 2, 128, "bf16"),
+    (64, [128, 127, 2], 8, 1, 64, "bf16"),
+    (300, [31, 33, 250, 1, 7], 4, 4, 128, "bf16"),
+])
+def test_small_trees(P, lens, Hq, Hkv, D, dtype):
+    w = make_inputs(make_shape(P, lens, Hq, Hkv, D, dtype=dtype, std=1.0 if dtype == "f32" else 0.5),
+                    seed=P * 1000 + len(lens))
+    _full_check(w, ALL)
+
+
+def test_sharp_attention_bf16():
+    # larger logits (std 2 on Q and K) exercise the running-maximum rescaling
+    w = make_inputs(make_shape(190, [70, 130, 9], 4, 2, 128, dtype="bf16", std=2.0), seed=77)
+    _full_check(w, ALL)
+
+
+def test_config2_forward_full():
+    w = config_inputs(2)
+    _full_check(w, ["o_p", "lse_p", "o_r", "lse_r"])
+
+
+def test_config3_one_kv_group_full_and_sum_rules():
+    w = config_inputs(3)
+    out = _full_check(w, ALL, kv_heads=[1])
+    e_v, e_k = sum_rules(w, out)
+    log(f"  sum rules: dV {e_v:.2e}, dK {e_k:.2e}")
+    assert e_v < 1e-2 and e_k < 1e-2
+
+
+def test_config3_bitwise_repeatable():
+    w = config_inputs(3)
+    t = upload(w)
+    a = run_path(w, t)
+    b = run_path(w, t)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def _sampled_check(cfg, n_prompt_rows, rows_per_branch, grad_branch_kv=0):
+    w = config_inputs(cfg)
+    s = w.shape
+    log(f"config {cfg}: P={s.P} T={s.T} lens={list(s.lens)}")
+    t = upload(w)
+    out = run_path(w, t)
+    rng = random.Random(cfg)
+    prow = sorted({0, 1, s.P - 1, *rng.sample(range(s.P), n_prompt_rows)})
+    off = s.offsets
+    rrow = set()
+    for i in range(s.G):
+        rrow |= {off[i], off[i + 1] - 1, (off[i] + off[i + 1]) // 2}
+        rrow |= set(rng.sample(range(off[i], off[i + 1]), rows_per_branch))
+    rrow = sorted(rrow)
+    ref = flattened_sampled_rows(w.q_p, w.k_p, w.v_p, w.q_r, w.k_r, w.v_r, w.offsets, prow, rrow,
+                                 do_p=w.do_p, do_r=w.do_r)
+    report = []
+    pi = torch.tensor(prow, device=out["o_p"].device)
+    ri = torch.tensor(rrow, device=out["o_p"].device)
+    compare("o_p", out["o_p"][pi], ref["o_p"], s.dtype, report)
+    compare("lse_p", out["lse_p"][:, pi], ref["lse_p"], s.dtype, report)
+    compare("dq_p", out["dq_p"][pi], ref["dq_p"], s.dtype, report)
+    compare("o_r", out["o_r"][ri], ref["o_r"], s.dtype, report)
+    compare("lse_r", out["lse_r"][:, ri], ref["lse_r"], s.dtype, report)
+    compare("dq_r", out["dq_r"][ri], ref["dq_r"], s.dtype, report)
+    # one branch's own K/V gradients (smallest branch), one kv group
+    b = min(range(s.G), key=lambda i: s.lens[i])
+    br = branch_response_grads(w.q_p, w.k_p, w.v_p, w.q_r, w.k_r, w.v_r, w.offsets, b, w.do_r,
+                               kv_heads=[grad_branch_kv])
+    sl = slice(off[b], off[b + 1])
+    compare("dk_r(branch)", out["dk_r"][sl, [grad_branch_kv]], br["dk_r"], s.dtype, report)
+    compare("dv_r(branch)", out["dv_r"][sl, [grad_branch_kv]], br["dv_r"], s.dtype, report)
+    log("  " + ", ".join(f"{n} {e:.1e}/{r:.1e}" for n, e, r, _ in report))
+    e_v, e_k = sum_rules(w, out)
+    log(f"  sum rules: dV {e_v:.2e}, dK {e_k:.2e}")
+    assert e_v < 1e-2 and e_k < 1e-2
+
+
+def test_config4_sampled_rows_branch_grads_sum_rules():
+    _sampled_check(4, n_prompt_rows=24, rows_per_branch=12)
+
+
+def test_config5_sampled_rows_branch_grads_sum_rules():
+    _sampled_check(5, n_prompt_rows=8, rows_per_branch=6, grad_branch_kv=7)
+
+
+def test_autograd_function_matches_entry_points():
+    from shared_prefix_attention_prompt_amd import shared_prefix_attention
+    w = make_inputs(make_shape(150, [40, 90], 4, 2, 128, dtype="bf16"), seed=5)
+    t = upload(w)
+    out = run_path(w, t)
+    leaves = {k: t[k].clone().requires_grad_(True) for k in ["q_p", "k_p", "v_p", "q_r", "k_r", "v_r"]}
+    o_p, o_r = shared_prefix_attention(leaves["q_p"], leaves["k_p"], leaves["v_p"], leaves["q_r"],
+                                       leaves["k_r"], leaves["v_r"], list(w.shape.offsets))
+    torch.autograd.backward([o_p, o_r], [t["do_p"], t["do_r"]])
+    assert torch.equal(o_p, out["o_p"]) and torch.equal(o_r, out["o_r"])
+    for k in ["q_p", "k_p", "v_p", "q_r", "k_r", "v_r"]:
+        assert torch.equal(leaves[k].grad, out["d" + k]), k
+
+
+def test_workspace_errors_are_reported_before_launch():
+    from shared_prefix_attention_prompt_amd import _lib
+    w = make_inputs(make_shape(16, [4, 4], 2, 2, 128, dtype="bf16"), seed=9)
+    t = upload(w)
+    dims, keep = _lib.make_dims(16, [0, 4, 8], 2, 2, 128, 128 ** -0.5, _lib.AUGTREE_BF16)
+    o = torch.empty_like(t["q_r"])
+    lse = torch.empty(2, 8, device="cuda:0")
+    need = _lib.workspace_bytes(dims, _lib.AUGTREE_OP_REPLAY_FWD)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    st = _lib.augtree_replay_fwd(dims, t["k_p"].data_ptr(), t["v_p"].data_ptr(), t["q_r"].data_ptr(),
+                                 t["k_r"].data_ptr(), t["v_r"].data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                 ws.data_ptr(), need - 1, 0)
+    assert st == _lib.AUGTREE_ERR_WORKSPACE
