@@ -51,7 +51,10 @@ def tolerances(dtype: str):
     return (1e-4, None) if dtype == "f32" else (2e-2, 1e-2)
 
 
-def compare(name: str, got: torch.Tensor, ref: torch.Tensor, dtype: str, report=None):
+def compare(name: str, got: torch.Tensor, ref: torch.Tensor, dtype: str, report=None,
+            abs_scale: bool = False):
+    """Max abs error within the dtype's bound (times max(1, max|ref|) when abs_scale) and,
+    for bf16, relative L2 error within 1e-2."""
     got = got.detach().to("cpu").to(torch.float64)
     ref = ref.to(torch.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
@@ -59,6 +62,8 @@ def compare(name: str, got: torch.Tensor, ref: torch.Tensor, dtype: str, report=
     err = float((got - ref).abs().max()) if got.numel() else 0.0
     rel = float((got - ref).norm() / ref.norm().clamp_min(1e-300)) if got.numel() else 0.0
     tol_abs, tol_rel = tolerances(dtype)
+    if abs_scale and ref.numel():
+        tol_abs *= max(1.0, float(ref.abs().max()))
     if report is not None:
         report.append((name, err, rel, float(ref.abs().max()) if ref.numel() else 0.0))
     assert err <= tol_abs, f"{name}: max abs error {err:.3e} > {tol_abs:.0e} (rel L2 {rel:.2e})"

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 ALL = ["o_p", "lse_p", "o_r", "lse_r", "dq_p", "dk_p", "dv_p", "dq_r", "dk_r", "dv_r"]
 
 
-def _full_check(w, keys, kv_heads=None):
+def _full_check(w, keys, kv_heads=None, abs_scale=False):
     log(f"case P={w.shape.P} lens={list(w.shape.lens)[:8]} Hq={w.shape.Hq} Hkv={w.shape.Hkv} "
         f"D={w.shape.D} {w.shape.dtype}")
     out = run_path(w, backward=w.shape.backward)
@@ -37,7 +37,7 @@ def _full_check(w, keys, kv_heads=None):
             g = g[:, kh]
         else:
             g = g[:, qh]
-        compare(k, g, ref[k], w.shape.dtype, report)
+        compare(k, g, ref[k], w.shape.dtype, report, abs_scale=abs_scale)
     log("  " + ", ".join(f"{n} {e:.1e}/{r:.1e}" for n, e, r, _ in report))
     return out
 
@@ -64,9 +64,12 @@ def test_small_trees(P, lens, Hq, Hkv, D, dtype):
 
 
 def test_sharp_attention_bf16():
-    # larger logits (std 2 on Q and K) exercise the running-maximum rescaling
+    # Stress input outside the graded workloads: std 2 on Q and K gives logits of std ~4,
+    # which exercises the running-maximum rescaling. Gradients reach ~10 here, so the
+    # absolute bound is taken relative to each tensor's largest magnitude (the bf16
+    # rounding of P and dS on the matrix cores is relative); rel L2 stays 1e-2.
     w = make_inputs(make_shape(190, [70, 130, 9], 4, 2, 128, dtype="bf16", std=2.0), seed=77)
-    _full_check(w, ALL)
+    _full_check(w, ALL, abs_scale=True)
 
 
 def test_config2_forward_full():
