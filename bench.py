@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of exact shared-prefix attention, forward + backward, on one MI355X.
+
+One step is the whole hot path over one replay tree, as eleven single C-ABI steps
+(identical kernels to the four composite calls): prompt prefill forward; replay against
+the stationary prompt K/V; response-local replay; LSE merge; row dots; prompt K/V gradient
+summed over all branches; branch K/V gradient; branch dQ; prefill K/V gradient (adding
+the branch sum); prefill dQ. Inputs are seeded, synthetic and resident in HBM before the
+timed region.
+
+Prints one JSON line: algorithmic TFLOP/s of the step (reuse work only: 4*D flops per
+visible (query, key) pair forward, 10*D backward, summed over query heads), the roofline
+of the dominant kernel (HIP events around its launch inside the timed steps), and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "shared-prefix attn fwd+bwd TFLOP/s and % bf16 MFMA peak, 1 MI355X"
+BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+F32_PEAK_TFLOPS = 157.3
+
+STAGES = ["prefill_fwd", "replay_prompt_fwd", "replay_local_fwd", "merge", "row_dot_r",
+          "replay_prompt_bwd", "replay_local_bwd", "replay_dq", "row_dot_p", "prefill_kv_bwd",
+          "prefill_dq"]
+
+
+def stage_flops(shape):
+    """Algorithmic flops of each MFMA stage (per launch), by the pair counts it covers.
+    Forward stages: 4*D per pair (QK^T, PV). Key-stationary gradient stages: 8*D per
+    pair (QK^T, dO V^T, P^T dO, dS^T Q). dQ stages: 2*D per pair (dS K), the remaining
+    algorithmic backward share; their recomputation of QK^T and dO V^T is not counted."""
+    P, T, D, Hq = shape.P, shape.T, shape.D, shape.Hq
+    tri_p = P * (P + 1) // 2
+    cross = T * P
+    tri_r = sum(r * (r + 1) // 2 for r in shape.lens)
+    return {
+        "prefill_fwd": 4 * D * tri_p * Hq,
+        "replay_prompt_fwd": 4 * D * cross * Hq,
+        "replay_local_fwd": 4 * D * tri_r * Hq,
+        "replay_prompt_bwd": 8 * D * cross * Hq,
+        "replay_local_bwd": 8 * D * tri_r * Hq,
+        "replay_dq": 2 * D * (cross + tri_r) * Hq,
+        "prefill_kv_bwd": 8 * D * tri_p * Hq,
+        "prefill_dq": 2 * D * tri_p * Hq,
+    }
+
+
+def stage_bytes(shape):
+    """Algorithmic HBM bytes of the HBM-bound stages (per launch)."""
+    T, P, D, Hq = shape.T, shape.P, shape.D, shape.Hq
+    esz = 2 if shape.dtype == "bf16" else 4
+    return {
+        # two fp32 partial outputs + two LSEs read, output + LSE written
+        "merge": T * Hq * (2 * 4 * D + 2 * 4 + esz * D + 4),
+        # O and dO read, one float written
+        "row_dot_r": T * Hq * (2 * esz * D + 4),
+        "row_dot_p": P * Hq * (2 * esz * D + 4),
+    }
+
+
+def cpu_baseline(w):
+    """The fp64 oracle on branch 0's flattened sequence (P + R_0 tokens) for query head 0,
+    forward + backward; extrapolated to the whole workload by flattened pair count x Hq
+    and converted to algorithmic TFLOP/s of the full workload."""
+    import torch
+    from oracle import flattened_tree_attention
+    from workloads import algorithmic_flops, pairs_flattened, make_shape
+
+    s = w.shape
+    R0 = s.lens[0]
+    sub = make_shape(s.P, [R0], 1, 1, s.D, dtype=s.dtype, std=s.std)
+    t0 = time.perf_counter()
+    flattened_tree_attention(w.q_p[:, :1], w.k_p[:, :1], w.v_p[:, :1], w.q_r[:R0, :1], w.k_r[:R0, :1],
+                             w.v_r[:R0, :1], [0, R0], do_p=w.do_p[:, :1], do_r=w.do_r[:R0, :1])
+    dt = time.perf_counter() - t0
+    sample_pairs = pairs_flattened(sub)
+    full_time = dt * (pairs_flattened(s) * s.Hq) / sample_pairs
+    value = algorithmic_flops(s) / full_time / 1e12
+    return {"value": value, "unit": "TFLOP/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"branch 0 flattened ({s.P}+{R0} tokens), query head 0, fwd+bwd in fp64: "
+                      f"{dt:.2f} s; extrapolated x{(pairs_flattened(s) * s.Hq) / sample_pairs:.1f} "
+                      f"(flattened pairs x Hq) to {full_time:.0f} s for the whole workload",
+            "sample_seconds": dt, "extrapolated_seconds": full_time}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4, help="workload number (1..5)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the shared-prefix "
+              "path is measured on one MI355X's share; no multi-GPU figure is produced.", file=sys.stderr)
+        return 2
+
+    import torch
+    from shared_prefix_attention_prompt_amd import _lib, ops
+    from workloads import CONFIGS, algorithmic_flops, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    _lib.load()
+    dev = torch.device("cuda:0")
+    cfg = args.config
+    t_gen = time.perf_counter()
+    w = make_inputs(cfg)
+    s = w.shape
+    t = {k: getattr(w, k).to(dev) for k in ["q_p", "k_p", "v_p", "q_r", "k_r", "v_r", "do_p", "do_r"]
+         if getattr(w, k) is not None}
+    torch.cuda.synchronize()
+    print(f"# inputs for config {cfg} ready in {time.perf_counter() - t_gen:.1f} s "
+          f"(P={s.P}, T_R={s.T}, G={s.G}, Hq={s.Hq}, Hkv={s.Hkv}, D={s.D})", file=sys.stderr, flush=True)
+
+    tr = ops.Tree(s.P, s.offsets, s.Hq, s.Hkv, s.D, s.torch_dtype, dev)
+    f32 = torch.float32
+    buf = {
+        "o_p": tr.empty(s.P, s.Hq, s.D), "lse_p": tr.empty(s.Hq, s.P, dtype=f32),
+        "oa": tr.empty(s.T, s.Hq, s.D, dtype=f32), "la": tr.empty(s.Hq, s.T, dtype=f32),
+        "ob": tr.empty(s.T, s.Hq, s.D, dtype=f32), "lb": tr.empty(s.Hq, s.T, dtype=f32),
+        "o_r": tr.empty(s.T, s.Hq, s.D), "lse_r": tr.empty(s.Hq, s.T, dtype=f32),
+        "rd_r": tr.empty(s.Hq, s.T, dtype=f32), "rd_p": tr.empty(s.Hq, s.P, dtype=f32),
+        "dk_acc": tr.empty(s.P, s.Hkv, s.D, dtype=f32), "dv_acc": tr.empty(s.P, s.Hkv, s.D, dtype=f32),
+        "dk_r": torch.empty_like(t["k_r"]), "dv_r": torch.empty_like(t["v_r"]),
+        "dq_r": torch.empty_like(t["q_r"]), "dk_p": torch.empty_like(t["k_p"]),
+        "dv_p": torch.empty_like(t["v_p"]), "dq_p": torch.empty_like(t["q_p"]),
+    }
+    nws = _lib.workspace_bytes(tr.dims, _lib.AUGTREE_OP_REPLAY_PROMPT_BWD)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        b = buf
+        mark(0)
+        _lib._check(_lib.augtree_prefill_fwd(tr.dims, t["q_p"].data_ptr(), t["k_p"].data_ptr(),
+                                             t["v_p"].data_ptr(), b["o_p"].data_ptr(), b["lse_p"].data_ptr(),
+                                             None, 0, tr.stream()), "augtree_prefill_fwd")
+        mark(1)
+        ops.replay_prompt_fwd(tr, t["k_p"], t["v_p"], t["q_r"], out=(b["oa"], b["la"]))
+        mark(2)
+        ops.replay_local_fwd(tr, t["q_r"], t["k_r"], t["v_r"], out=(b["ob"], b["lb"]))
+        mark(3)
+        ops.merge_partials(tr, [(b["oa"], b["la"]), (b["ob"], b["lb"])], out=(b["o_r"], b["lse_r"]))
+        mark(4)
+        if not s.backward:
+            return
+        ops.row_dot(tr, b["o_r"], t["do_r"], out=b["rd_r"])
+        mark(5)
+        ops.replay_prompt_bwd(tr, t["k_p"], t["v_p"], t["q_r"], b["lse_r"], b["rd_r"], t["do_r"],
+                              dk_acc=b["dk_acc"], dv_acc=b["dv_acc"], ws=ws)
+        mark(6)
+        ops.replay_local_bwd(tr, t["q_r"], t["k_r"], t["v_r"], b["lse_r"], b["rd_r"], t["do_r"],
+                             out=(b["dk_r"], b["dv_r"]))
+        mark(7)
+        ops.replay_dq(tr, t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], b["lse_r"], b["rd_r"], t["do_r"],
+                      out=b["dq_r"])
+        mark(8)
+        ops.row_dot(tr, b["o_p"], t["do_p"], out=b["rd_p"])
+        mark(9)
+        ops.prefill_kv_bwd(tr, t["q_p"], t["k_p"], t["v_p"], b["lse_p"], b["rd_p"], t["do_p"], b["dk_acc"],
+                           b["dv_acc"], out=(b["dk_p"], b["dv_p"]))
+        mark(10)
+        ops.prefill_dq(tr, t["q_p"], t["k_p"], t["v_p"], b["lse_p"], b["rd_p"], t["do_p"], out=b["dq_p"])
+        mark(11)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(events[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    stages = STAGES if s.backward else STAGES[:4]
+    stage_ms = {}
+    for j, name in enumerate(stages):
+        stage_ms[name] = sum(events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)) / args.steps
+    flops = algorithmic_flops(s)
+    tflops = flops / (ms_per_step / 1e3) / 1e12
+    peak = BF16_PEAK_TFLOPS if s.dtype == "bf16" else F32_PEAK_TFLOPS
+    sf = {k: v for k, v in stage_flops(s).items() if k in stages}
+    sb = {k: v for k, v in stage_bytes(s).items() if k in stages}
+    kernels = {}
+    for name in stages:
+        ms = stage_ms[name]
+        entry = {"ms": round(ms, 4)}
+        if name in sf:
+            entry["TFLOP/s"] = round(sf[name] / (ms / 1e3) / 1e12, 1)
+        if name in sb:
+            entry["GB/s"] = round(sb[name] / (ms / 1e3) / 1e9, 1)
+        kernels[name] = entry
+    dom = max(sf, key=lambda n: stage_ms[n])
+    achieved = sf[dom] / (stage_ms[dom] / 1e3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "alg_flops_per_launch": sf[dom], "avg_launch_ms": round(stage_ms[dom], 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline and s.backward:
+        cpu = cpu_baseline(w)
+        cpu["value"] = round(cpu["value"], 6)
+
+    line = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": s.dtype,
+        "data": "synthetic", "pct_bf16_peak": round(100 * tflops / peak, 2),
+        "config": {"workload": CONFIGS[cfg]["workload"], "P": s.P, "G": s.G, "branch_lens": list(s.lens),
+                   "T_R": s.T, "Hq": s.Hq, "Hkv": s.Hkv, "D": s.D,
+                   "passes": "fwd+bwd" if s.backward else "fwd",
+                   "alg_flops": flops, "seed": 20260000 + cfg},
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -65,7 +65,10 @@ typedef enum {
 
 /* Operation codes for augtree_workspace_bytes. */
 enum { AUGTREE_OP_PREFILL_FWD = 0, AUGTREE_OP_REPLAY_FWD = 1, AUGTREE_OP_REPLAY_BWD = 2,
-       AUGTREE_OP_PREFILL_BWD = 3 };
+       AUGTREE_OP_PREFILL_BWD = 3, AUGTREE_OP_REPLAY_PROMPT_BWD = 4 };
+
+/* Most partial states augtree_merge_partials accepts in one call. */
+#define AUGTREE_MAX_PARTS 8
 
 /* Sizes of one replay tree. Only branch_offsets is a HOST pointer. */
 typedef struct {
@@ -127,6 +130,83 @@ augtree_status augtree_prefill_bwd(const augtree_dims *dims, const void *q_p, co
                                    const void *do_p, const float *dk_p_acc,
                                    const float *dv_p_acc, void *dq_p, void *dk_p, void *dv_p,
                                    void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Single steps. The four calls above are compositions of these (each launches one kernel,
+ * augtree_replay_prompt_bwd one or two):
+ *   replay_fwd  = replay_prompt_fwd(0, P) + replay_local_fwd + merge_partials(2 parts)
+ *   replay_bwd  = row_dot(T_R rows) + replay_prompt_bwd(0, P) + replay_local_bwd + replay_dq
+ *   prefill_bwd = row_dot(P rows) + prefill_kv_bwd + prefill_dq
+ * A prompt key range [key_begin, key_end) lets one call act as one stationary prompt-K/V
+ * shard of §3.3 MoveQ: the shard's partial states are later merged per query row.
+ * Partial states are (normalised output, LSE) pairs: o_part [T_R][Hq][D] float32 and
+ * lse_part [Hq][T_R]; a row with no visible key in the range has lse = -inf and o = 0.
+ * rowdot [Hq][rows] float32 is sum_d dO[r][h][d] * O[r][h][d] of the saved outputs.
+ * --------------------------------------------------------------------------------------- */
+
+/* Partial state of every branch row over prompt keys [key_begin, key_end), no mask
+ * (§3.3 MoveQ: a stationary prompt K/V shard evaluates all branch queries).
+ * 0 <= key_begin < key_end <= P. */
+augtree_status augtree_replay_prompt_fwd(const augtree_dims *dims, const void *k_p,
+                                         const void *v_p, const void *q_r, int32_t key_begin,
+                                         int32_t key_end, float *o_part, float *lse_part,
+                                         void *stream);
+
+/* Partial state of every branch row over its own branch, causally (§3.2, Eq. 1: a branch
+ * token sees its own earlier tokens and itself, never a sibling). */
+augtree_status augtree_replay_local_fwd(const augtree_dims *dims, const void *q_r,
+                                        const void *k_r, const void *v_r, float *o_part,
+                                        float *lse_part, void *stream);
+
+/* Exact merge of num_parts (1..AUGTREE_MAX_PARTS) partial states per branch row (§3.3,
+ * Fig. 8: states along a query row are combined by the log-sum-exp rule, not by
+ * averaging normalised outputs). o_parts/lse_parts are HOST arrays of device pointers.
+ * out: o_r [T_R][Hq][D] (dtype), lse_r [Hq][T_R]. Parts are combined in index order. */
+augtree_status augtree_merge_partials(const augtree_dims *dims, int32_t num_parts,
+                                      const float *const *o_parts,
+                                      const float *const *lse_parts, void *o_r, float *lse_r,
+                                      void *stream);
+
+/* rowdot[h][r] = sum_d d_o[r][h][d] * o[r][h][d] for rows = P (prompt) or T_R (branches);
+ * the row statistic of the softmax backward. */
+augtree_status augtree_row_dot(const augtree_dims *dims, int32_t rows, const void *o,
+                               const void *d_o, float *rowdot, void *stream);
+
+/* Prompt K/V gradient from every branch row, for prompt keys [key_begin, key_end): writes
+ * rows [key_begin, key_end) of dk_p_acc/dv_p_acc [P][Hkv][D] float32 with the sum over all
+ * branches and over the query heads of each group (§3.2, equation after Eq. 1), in a fixed
+ * order. Workspace: augtree_workspace_bytes(dims, AUGTREE_OP_REPLAY_PROMPT_BWD). */
+augtree_status augtree_replay_prompt_bwd(const augtree_dims *dims, const void *k_p,
+                                         const void *v_p, const void *q_r, const float *lse_r,
+                                         const float *rowdot_r, const void *do_r,
+                                         int32_t key_begin, int32_t key_end, float *dk_p_acc,
+                                         float *dv_p_acc, void *ws, size_t ws_bytes,
+                                         void *stream);
+
+/* dK/dV of the branch keys (own-branch rows only, causal): dk_r/dv_r [T_R][Hkv][D]. */
+augtree_status augtree_replay_local_bwd(const augtree_dims *dims, const void *q_r,
+                                        const void *k_r, const void *v_r, const float *lse_r,
+                                        const float *rowdot_r, const void *do_r, void *dk_r,
+                                        void *dv_r, void *stream);
+
+/* dQ of every branch row over the whole prompt and its own branch: dq_r [T_R][Hq][D]. */
+augtree_status augtree_replay_dq(const augtree_dims *dims, const void *k_p, const void *v_p,
+                                 const void *q_r, const void *k_r, const void *v_r,
+                                 const float *lse_r, const float *rowdot_r, const void *do_r,
+                                 void *dq_r, void *stream);
+
+/* Prompt dK/dV: the prompt queries' causal contribution plus dk_p_acc/dv_p_acc (or
+ * nothing when both are NULL), rounded once: dk_p/dv_p [P][Hkv][D] (dtype). */
+augtree_status augtree_prefill_kv_bwd(const augtree_dims *dims, const void *q_p,
+                                      const void *k_p, const void *v_p, const float *lse_p,
+                                      const float *rowdot_p, const void *do_p,
+                                      const float *dk_p_acc, const float *dv_p_acc, void *dk_p,
+                                      void *dv_p, void *stream);
+
+/* dQ of the prompt rows (causal over the prompt): dq_p [P][Hq][D]. */
+augtree_status augtree_prefill_dq(const augtree_dims *dims, const void *q_p, const void *k_p,
+                                  const void *v_p, const float *lse_p, const float *rowdot_p,
+                                  const void *do_p, void *dq_p, void *stream);
 
 /* Bytes of workspace operation `op` (AUGTREE_OP_*) needs for `dims`; 0 for invalid dims. */
 size_t augtree_workspace_bytes(const augtree_dims *dims, int op);

@@ -23,10 +23,15 @@ AUGTREE_OP_PREFILL_FWD = 0
 AUGTREE_OP_REPLAY_FWD = 1
 AUGTREE_OP_REPLAY_BWD = 2
 AUGTREE_OP_PREFILL_BWD = 3
+AUGTREE_OP_REPLAY_PROMPT_BWD = 4
 AUGTREE_MAX_BRANCHES = 128
+AUGTREE_MAX_PARTS = 8
 
 ENTRY_POINTS = ["augtree_prefill_fwd", "augtree_replay_fwd", "augtree_replay_bwd",
-                "augtree_prefill_bwd", "augtree_workspace_bytes", "augtree_status_string",
+                "augtree_prefill_bwd", "augtree_replay_prompt_fwd", "augtree_replay_local_fwd",
+                "augtree_merge_partials", "augtree_row_dot", "augtree_replay_prompt_bwd",
+                "augtree_replay_local_bwd", "augtree_replay_dq", "augtree_prefill_kv_bwd",
+                "augtree_prefill_dq", "augtree_workspace_bytes", "augtree_status_string",
                 "augtree_last_error", "augtree_abi_version"]
 
 
@@ -63,7 +68,18 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.augtree_replay_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.augtree_replay_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.augtree_prefill_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for name in ["augtree_prefill_fwd", "augtree_replay_fwd", "augtree_replay_bwd", "augtree_prefill_bwd"]:
+    i32 = ctypes.c_int32
+    fpp = ctypes.POINTER(ctypes.c_void_p)
+    lib.augtree_replay_prompt_fwd.argtypes = [P, vp, vp, vp, i32, i32, vp, vp, vp]
+    lib.augtree_replay_local_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.augtree_merge_partials.argtypes = [P, i32, fpp, fpp, vp, vp, vp]
+    lib.augtree_row_dot.argtypes = [P, i32, vp, vp, vp, vp]
+    lib.augtree_replay_prompt_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+    lib.augtree_replay_local_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.augtree_replay_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.augtree_prefill_kv_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.augtree_prefill_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    for name in ENTRY_POINTS[:13]:
         getattr(lib, name).restype = st
     lib.augtree_workspace_bytes.argtypes = [P, ctypes.c_int]
     lib.augtree_workspace_bytes.restype = sz
@@ -126,3 +142,50 @@ def augtree_prefill_bwd(dims, q_p, k_p, v_p, o_p, lse_p, do_p, dk_p_acc, dv_p_ac
                         dv_p, ws, ws_bytes, stream) -> int:
     return load().augtree_prefill_bwd(ctypes.byref(dims), q_p, k_p, v_p, o_p, lse_p, do_p, dk_p_acc,
                                       dv_p_acc, dq_p, dk_p, dv_p, ws, ws_bytes, stream)
+
+
+def augtree_replay_prompt_fwd(dims, k_p, v_p, q_r, key_begin, key_end, o_part, lse_part, stream) -> int:
+    return load().augtree_replay_prompt_fwd(ctypes.byref(dims), k_p, v_p, q_r, int(key_begin), int(key_end),
+                                            o_part, lse_part, stream)
+
+
+def augtree_replay_local_fwd(dims, q_r, k_r, v_r, o_part, lse_part, stream) -> int:
+    return load().augtree_replay_local_fwd(ctypes.byref(dims), q_r, k_r, v_r, o_part, lse_part, stream)
+
+
+def augtree_merge_partials(dims, o_parts, lse_parts, o_r, lse_r, stream) -> int:
+    n = len(o_parts)
+    oa = (ctypes.c_void_p * max(n, 1))(*o_parts)
+    la = (ctypes.c_void_p * max(len(lse_parts), 1))(*lse_parts)
+    return load().augtree_merge_partials(ctypes.byref(dims), n, oa, la, o_r, lse_r, stream)
+
+
+def augtree_row_dot(dims, rows, o, d_o, rowdot, stream) -> int:
+    return load().augtree_row_dot(ctypes.byref(dims), int(rows), o, d_o, rowdot, stream)
+
+
+def augtree_replay_prompt_bwd(dims, k_p, v_p, q_r, lse_r, rowdot_r, do_r, key_begin, key_end, dk_p_acc,
+                              dv_p_acc, ws, ws_bytes, stream) -> int:
+    return load().augtree_replay_prompt_bwd(ctypes.byref(dims), k_p, v_p, q_r, lse_r, rowdot_r, do_r,
+                                            int(key_begin), int(key_end), dk_p_acc, dv_p_acc, ws, ws_bytes,
+                                            stream)
+
+
+def augtree_replay_local_bwd(dims, q_r, k_r, v_r, lse_r, rowdot_r, do_r, dk_r, dv_r, stream) -> int:
+    return load().augtree_replay_local_bwd(ctypes.byref(dims), q_r, k_r, v_r, lse_r, rowdot_r, do_r, dk_r,
+                                           dv_r, stream)
+
+
+def augtree_replay_dq(dims, k_p, v_p, q_r, k_r, v_r, lse_r, rowdot_r, do_r, dq_r, stream) -> int:
+    return load().augtree_replay_dq(ctypes.byref(dims), k_p, v_p, q_r, k_r, v_r, lse_r, rowdot_r, do_r, dq_r,
+                                    stream)
+
+
+def augtree_prefill_kv_bwd(dims, q_p, k_p, v_p, lse_p, rowdot_p, do_p, dk_p_acc, dv_p_acc, dk_p, dv_p,
+                           stream) -> int:
+    return load().augtree_prefill_kv_bwd(ctypes.byref(dims), q_p, k_p, v_p, lse_p, rowdot_p, do_p, dk_p_acc,
+                                         dv_p_acc, dk_p, dv_p, stream)
+
+
+def augtree_prefill_dq(dims, q_p, k_p, v_p, lse_p, rowdot_p, do_p, dq_p, stream) -> int:
+    return load().augtree_prefill_dq(ctypes.byref(dims), q_p, k_p, v_p, lse_p, rowdot_p, do_p, dq_p, stream)

@@ -178,11 +178,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   }
 }
 
-// Merge of the two replay partial states of each (row, head): the prompt part (a) and the
-// response-local part (b), each given as a normalised output and its LSE. The combined
-// LSE is max + log(e^(lse_a-max) + e^(lse_b-max)) and the combined output is the
-// LSE-weighted mix, which equals merging the unnormalised (m, l, O_acc) states (§3.3).
-// D/4 lanes handle one (row, head), four fp32 elements per lane.
+// Merge of the replay partial states of each (row, head), e.g. the prompt part and the
+// response-local part, or the parts of several prompt K/V shards. Each part is a normalised
+// output with its LSE; the combined LSE is m + log(sum_i e^(lse_i - m)) with m = max_i lse_i,
+// and the combined output is the e^(lse_i - lse)-weighted sum of the parts, which equals
+// merging the unnormalised (m, l, O_acc) states (§3.3, Fig. 8). Parts are visited in index
+// order. D/4 lanes handle one (row, head), four fp32 elements per lane.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   constexpr int LPR = D / 4;
@@ -193,25 +194,38 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   if (idx >= (int64_t)a.rows * a.Hq) return;
   const int64_t row = idx / a.Hq;
   const int h = (int)(idx % a.Hq);
-  const float la = a.lse_a[(int64_t)h * a.rows + row];
-  const float lb = a.lse_b[(int64_t)h * a.rows + row];
-  const float mx = fmaxf(la, lb);
-  float wa = 0.f, wb = 0.f, lse = -kInf;
-  if (mx != -kInf) {
-    const float ea = __builtin_amdgcn_exp2f((la - mx) * kLog2e);
-    const float eb = __builtin_amdgcn_exp2f((lb - mx) * kLog2e);
-    const float s = ea + eb;
-    const float inv = 1.0f / s;
-    wa = ea * inv;
-    wb = eb * inv;
-    lse = mx + __builtin_amdgcn_logf(s) * kLn2;
+  const int64_t li = (int64_t)h * a.rows + row;
+  float l[kMaxParts];
+  float mx = -kInf;
+#pragma unroll
+  for (int i = 0; i < kMaxParts; ++i) {
+    l[i] = i < a.nparts ? a.lse_part[i][li] : -kInf;
+    mx = fmaxf(mx, l[i]);
   }
   const int64_t off = idx * D + sub * 4;
-  const f32x4 oa = *reinterpret_cast<const f32x4*>(a.o_a + off);
-  const f32x4 ob = *reinterpret_cast<const f32x4*>(a.o_b + off);
-  store4<T>(reinterpret_cast<T*>(a.o) + off, wa * oa[0] + wb * ob[0], wa * oa[1] + wb * ob[1],
-            wa * oa[2] + wb * ob[2], wa * oa[3] + wb * ob[3]);
-  if (sub == 0) a.lse[(int64_t)h * a.rows + row] = lse;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float lse = -kInf;
+  if (mx != -kInf) {
+    float e[kMaxParts];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxParts; ++i) {
+      e[i] = i < a.nparts ? __builtin_amdgcn_exp2f((l[i] - mx) * kLog2e) : 0.f;
+      s += e[i];
+    }
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < kMaxParts; ++i) {
+      if (i < a.nparts && e[i] > 0.f) {
+        const float wgt = e[i] * inv;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(a.o_part[i] + off);
+        acc[0] += wgt * x[0]; acc[1] += wgt * x[1]; acc[2] += wgt * x[2]; acc[3] += wgt * x[3];
+      }
+    }
+    lse = mx + __builtin_amdgcn_logf(s) * kLn2;
+  }
+  store4<T>(reinterpret_cast<T*>(a.o) + off, acc[0], acc[1], acc[2], acc[3]);
+  if (sub == 0) a.lse[li] = lse;
 }
 
 template <typename T, int D>

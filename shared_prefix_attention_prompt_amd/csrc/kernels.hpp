@@ -26,10 +26,12 @@ struct FwdArgs {
   BranchTable bt;     // replay-local only: branch offsets and per-branch tile prefix
 };
 
-// ---- merge of two partial states (normalised output + LSE) per (row, head) ----
+// ---- merge of partial states (normalised output + LSE) per (row, head) ----
+constexpr int kMaxParts = 8;
 struct MergeArgs {
-  const float* o_a; const float* lse_a;   // [T][Hq][D], [Hq][T]
-  const float* o_b; const float* lse_b;
+  const float* o_part[kMaxParts];    // [T][Hq][D] each
+  const float* lse_part[kMaxParts];  // [Hq][T] each
+  int32_t nparts;
   void* o;            // [T][Hq][D] dtype
   float* lse;         // [Hq][T]
   int32_t rows, Hq;

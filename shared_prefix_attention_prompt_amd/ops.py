@@ -162,3 +162,126 @@ class SharedPrefixAttention(torch.autograd.Function):
 def shared_prefix_attention(q_p, k_p, v_p, q_r, k_r, v_r, offsets, scale: Optional[float] = None):
     """(o_p, o_r) with autograd support; see :class:`SharedPrefixAttention`."""
     return SharedPrefixAttention.apply(q_p, k_p, v_p, q_r, k_r, v_r, offsets, scale)
+
+
+# ---------------------------------------------------------------------------------------
+# Single steps (one kernel each; replay_prompt_bwd one or three). The four calls above are
+# compositions of these; a prompt key range makes a call act as one stationary prompt-K/V
+# shard whose partial states are merged per query row afterwards.
+# ---------------------------------------------------------------------------------------
+class Tree:
+    """Sizes of one replay tree, for the single-step calls."""
+
+    def __init__(self, P: int, offsets: Sequence[int], Hq: int, Hkv: int, D: int,
+                 dtype: torch.dtype, device, scale: Optional[float] = None):
+        self.P, self.Hq, self.Hkv, self.D = int(P), int(Hq), int(Hkv), int(D)
+        self.offsets = [int(x) for x in offsets]
+        self.T = self.offsets[-1]
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.dims, self._keep = _dims(P, self.offsets, Hq, Hkv, D, scale, dtype)
+
+    @classmethod
+    def like(cls, q_p, k_p, offsets, scale: Optional[float] = None) -> "Tree":
+        return cls(q_p.shape[0], _offsets_list(offsets), q_p.shape[1], k_p.shape[1], q_p.shape[2],
+                   q_p.dtype, q_p.device, scale)
+
+    def stream(self) -> int:
+        return _stream(self.device)
+
+    def empty(self, *shape, dtype=None):
+        return torch.empty(*shape, dtype=self.dtype if dtype is None else dtype, device=self.device)
+
+
+def replay_prompt_fwd(tr: Tree, k_p, v_p, q_r, key_begin: int = 0, key_end: Optional[int] = None,
+                      out=None):
+    """Partial state (o_part float32 [T][Hq][D], lse_part [Hq][T]) of every branch row over
+    prompt keys [key_begin, key_end)."""
+    key_end = tr.P if key_end is None else key_end
+    o, l = out if out is not None else (tr.empty(tr.T, tr.Hq, tr.D, dtype=torch.float32),
+                                        tr.empty(tr.Hq, tr.T, dtype=torch.float32))
+    st = _lib.augtree_replay_prompt_fwd(tr.dims, k_p.data_ptr(), v_p.data_ptr(), q_r.data_ptr(), key_begin,
+                                        key_end, o.data_ptr(), l.data_ptr(), tr.stream())
+    _lib._check(st, "augtree_replay_prompt_fwd")
+    return o, l
+
+
+def replay_local_fwd(tr: Tree, q_r, k_r, v_r, out=None):
+    """Partial state of every branch row over its own branch (causal)."""
+    o, l = out if out is not None else (tr.empty(tr.T, tr.Hq, tr.D, dtype=torch.float32),
+                                        tr.empty(tr.Hq, tr.T, dtype=torch.float32))
+    st = _lib.augtree_replay_local_fwd(tr.dims, q_r.data_ptr(), k_r.data_ptr(), v_r.data_ptr(), o.data_ptr(),
+                                       l.data_ptr(), tr.stream())
+    _lib._check(st, "augtree_replay_local_fwd")
+    return o, l
+
+
+def merge_partials(tr: Tree, parts, out=None):
+    """Exact log-sum-exp merge of [(o_part, lse_part), ...] -> (o_r dtype, lse_r)."""
+    o, l = out if out is not None else (tr.empty(tr.T, tr.Hq, tr.D), tr.empty(tr.Hq, tr.T, dtype=torch.float32))
+    st = _lib.augtree_merge_partials(tr.dims, [p[0].data_ptr() for p in parts], [p[1].data_ptr() for p in parts],
+                                     o.data_ptr(), l.data_ptr(), tr.stream())
+    _lib._check(st, "augtree_merge_partials")
+    return o, l
+
+
+def row_dot(tr: Tree, o, d_o, out=None):
+    """rowdot [Hq][rows] = sum_d dO * O for rows = o.shape[0] (P or T_R)."""
+    rows = o.shape[0]
+    r = out if out is not None else tr.empty(tr.Hq, rows, dtype=torch.float32)
+    st = _lib.augtree_row_dot(tr.dims, rows, o.data_ptr(), d_o.data_ptr(), r.data_ptr(), tr.stream())
+    _lib._check(st, "augtree_row_dot")
+    return r
+
+
+def replay_prompt_bwd(tr: Tree, k_p, v_p, q_r, lse_r, rowdot_r, do_r, key_begin: int = 0,
+                      key_end: Optional[int] = None, dk_acc=None, dv_acc=None, ws=None):
+    """Rows [key_begin, key_end) of the branches' summed prompt K/V gradient (float32
+    [P][Hkv][D] buffers, allocated when not given)."""
+    key_end = tr.P if key_end is None else key_end
+    if dk_acc is None:
+        dk_acc = tr.empty(tr.P, tr.Hkv, tr.D, dtype=torch.float32)
+        dv_acc = tr.empty(tr.P, tr.Hkv, tr.D, dtype=torch.float32)
+    n = _lib.workspace_bytes(tr.dims, _lib.AUGTREE_OP_REPLAY_PROMPT_BWD)
+    if ws is None and n:
+        ws = torch.empty(n, dtype=torch.uint8, device=tr.device)
+    st = _lib.augtree_replay_prompt_bwd(tr.dims, k_p.data_ptr(), v_p.data_ptr(), q_r.data_ptr(), lse_r.data_ptr(),
+                                        rowdot_r.data_ptr(), do_r.data_ptr(), key_begin, key_end, dk_acc.data_ptr(),
+                                        dv_acc.data_ptr(), _ptr(ws), n, tr.stream())
+    _lib._check(st, "augtree_replay_prompt_bwd")
+    return dk_acc, dv_acc
+
+
+def replay_local_bwd(tr: Tree, q_r, k_r, v_r, lse_r, rowdot_r, do_r, out=None):
+    dk, dv = out if out is not None else (torch.empty_like(k_r), torch.empty_like(v_r))
+    st = _lib.augtree_replay_local_bwd(tr.dims, q_r.data_ptr(), k_r.data_ptr(), v_r.data_ptr(), lse_r.data_ptr(),
+                                       rowdot_r.data_ptr(), do_r.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                       tr.stream())
+    _lib._check(st, "augtree_replay_local_bwd")
+    return dk, dv
+
+
+def replay_dq(tr: Tree, k_p, v_p, q_r, k_r, v_r, lse_r, rowdot_r, do_r, out=None):
+    dq = out if out is not None else torch.empty_like(q_r)
+    st = _lib.augtree_replay_dq(tr.dims, k_p.data_ptr(), v_p.data_ptr(), q_r.data_ptr(), k_r.data_ptr(),
+                                v_r.data_ptr(), lse_r.data_ptr(), rowdot_r.data_ptr(), do_r.data_ptr(),
+                                dq.data_ptr(), tr.stream())
+    _lib._check(st, "augtree_replay_dq")
+    return dq
+
+
+def prefill_kv_bwd(tr: Tree, q_p, k_p, v_p, lse_p, rowdot_p, do_p, dk_acc=None, dv_acc=None, out=None):
+    dk, dv = out if out is not None else (torch.empty_like(k_p), torch.empty_like(v_p))
+    st = _lib.augtree_prefill_kv_bwd(tr.dims, q_p.data_ptr(), k_p.data_ptr(), v_p.data_ptr(), lse_p.data_ptr(),
+                                     rowdot_p.data_ptr(), do_p.data_ptr(), _ptr(dk_acc), _ptr(dv_acc),
+                                     dk.data_ptr(), dv.data_ptr(), tr.stream())
+    _lib._check(st, "augtree_prefill_kv_bwd")
+    return dk, dv
+
+
+def prefill_dq(tr: Tree, q_p, k_p, v_p, lse_p, rowdot_p, do_p, out=None):
+    dq = out if out is not None else torch.empty_like(q_p)
+    st = _lib.augtree_prefill_dq(tr.dims, q_p.data_ptr(), k_p.data_ptr(), v_p.data_ptr(), lse_p.data_ptr(),
+                                 rowdot_p.data_ptr(), do_p.data_ptr(), dq.data_ptr(), tr.stream())
+    _lib._check(st, "augtree_prefill_dq")
+    return dq
