@@ -138,7 +138,7 @@ def main() -> int:
         "dq_r": torch.empty_like(t["q_r"]), "dk_p": torch.empty_like(t["k_p"]),
         "dv_p": torch.empty_like(t["v_p"]), "dq_p": torch.empty_like(t["q_p"]),
     }
-    nws = _lib.workspace_bytes(tr.dims, _lib.AUGTREE_OP_REPLAY_PROMPT_BWD)
+    nws = max(_lib.workspace_bytes(tr.dims, op) for op in range(11))
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -150,11 +150,11 @@ def main() -> int:
         mark(0)
         _lib._check(_lib.augtree_prefill_fwd(tr.dims, t["q_p"].data_ptr(), t["k_p"].data_ptr(),
                                              t["v_p"].data_ptr(), b["o_p"].data_ptr(), b["lse_p"].data_ptr(),
-                                             None, 0, tr.stream()), "augtree_prefill_fwd")
+                                             ws.data_ptr(), ws.numel(), tr.stream()), "augtree_prefill_fwd")
         mark(1)
-        ops.replay_prompt_fwd(tr, t["k_p"], t["v_p"], t["q_r"], out=(b["oa"], b["la"]))
+        ops.replay_prompt_fwd(tr, t["k_p"], t["v_p"], t["q_r"], out=(b["oa"], b["la"]), ws=ws)
         mark(2)
-        ops.replay_local_fwd(tr, t["q_r"], t["k_r"], t["v_r"], out=(b["ob"], b["lb"]))
+        ops.replay_local_fwd(tr, t["q_r"], t["k_r"], t["v_r"], out=(b["ob"], b["lb"]), ws=ws)
         mark(3)
         ops.merge_partials(tr, [(b["oa"], b["la"]), (b["ob"], b["lb"])], out=(b["o_r"], b["lse_r"]))
         mark(4)
@@ -166,17 +166,17 @@ def main() -> int:
                               dk_acc=b["dk_acc"], dv_acc=b["dv_acc"], ws=ws)
         mark(6)
         ops.replay_local_bwd(tr, t["q_r"], t["k_r"], t["v_r"], b["lse_r"], b["rd_r"], t["do_r"],
-                             out=(b["dk_r"], b["dv_r"]))
+                             out=(b["dk_r"], b["dv_r"]), ws=ws)
         mark(7)
         ops.replay_dq(tr, t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], b["lse_r"], b["rd_r"], t["do_r"],
-                      out=b["dq_r"])
+                      out=b["dq_r"], ws=ws)
         mark(8)
         ops.row_dot(tr, b["o_p"], t["do_p"], out=b["rd_p"])
         mark(9)
         ops.prefill_kv_bwd(tr, t["q_p"], t["k_p"], t["v_p"], b["lse_p"], b["rd_p"], t["do_p"], b["dk_acc"],
-                           b["dv_acc"], out=(b["dk_p"], b["dv_p"]))
+                           b["dv_acc"], out=(b["dk_p"], b["dv_p"]), ws=ws)
         mark(10)
-        ops.prefill_dq(tr, t["q_p"], t["k_p"], t["v_p"], b["lse_p"], b["rd_p"], t["do_p"], out=b["dq_p"])
+        ops.prefill_dq(tr, t["q_p"], t["k_p"], t["v_p"], b["lse_p"], b["rd_p"], t["do_p"], out=b["dq_p"], ws=ws)
         mark(11)
 
     for _ in range(args.warmup):

@@ -39,6 +39,11 @@
  *
  * Results are bitwise reproducible for identical inputs and dims: no floating-point
  * atomics are used anywhere; every reduction runs in a fixed order.
+ *
+ * Workspaces: every entry point that takes one writes transposed copies of some of its
+ * operands there (head_dim-major, sequence-contiguous, each branch padded to 64 positions),
+ * plus the partial results named at the entry point. augtree_workspace_bytes gives the size;
+ * the pointer must be 256-byte aligned. The workspace holds nothing between calls.
  */
 #ifndef AUGTREE_H
 #define AUGTREE_H
@@ -50,7 +55,7 @@
 extern "C" {
 #endif
 
-#define AUGTREE_ABI_VERSION 1
+#define AUGTREE_ABI_VERSION 2
 #define AUGTREE_MAX_BRANCHES 128
 
 typedef enum { AUGTREE_F32 = 0, AUGTREE_BF16 = 1 } augtree_dtype;
@@ -63,9 +68,12 @@ typedef enum {
   AUGTREE_ERR_HIP = 4               /* a HIP launch or runtime call failed */
 } augtree_status;
 
-/* Operation codes for augtree_workspace_bytes. */
+/* Operation codes for augtree_workspace_bytes: one per entry point that takes a workspace. */
 enum { AUGTREE_OP_PREFILL_FWD = 0, AUGTREE_OP_REPLAY_FWD = 1, AUGTREE_OP_REPLAY_BWD = 2,
-       AUGTREE_OP_PREFILL_BWD = 3, AUGTREE_OP_REPLAY_PROMPT_BWD = 4 };
+       AUGTREE_OP_PREFILL_BWD = 3, AUGTREE_OP_REPLAY_PROMPT_BWD = 4,
+       AUGTREE_OP_REPLAY_PROMPT_FWD = 5, AUGTREE_OP_REPLAY_LOCAL_FWD = 6,
+       AUGTREE_OP_REPLAY_LOCAL_BWD = 7, AUGTREE_OP_REPLAY_DQ = 8, AUGTREE_OP_PREFILL_KV_BWD = 9,
+       AUGTREE_OP_PREFILL_DQ = 10 };
 
 /* Most partial states augtree_merge_partials accepts in one call. */
 #define AUGTREE_MAX_PARTS 8
@@ -87,7 +95,7 @@ typedef struct {
 /* Causal attention of the prompt over itself, computed once for all branches (§3.2,
  * shared prompt prefill; attention definition §2.2).
  * in:  q_p [P][Hq][D], k_p/v_p [P][Hkv][D]   out: o_p [P][Hq][D], lse_p [Hq][P].
- * Workspace: augtree_workspace_bytes(dims, AUGTREE_OP_PREFILL_FWD) (0: ws may be NULL). */
+ * Workspace: augtree_workspace_bytes(dims, AUGTREE_OP_PREFILL_FWD) (a transposed V). */
 augtree_status augtree_prefill_fwd(const augtree_dims *dims, const void *q_p, const void *k_p,
                                    const void *v_p, void *o_p, float *lse_p, void *ws,
                                    size_t ws_bytes, void *stream);
@@ -98,7 +106,7 @@ augtree_status augtree_prefill_fwd(const augtree_dims *dims, const void *q_p, co
  * two states are merged by the log-sum-exp rule of §3.3 (Fig. 8).
  * in:  k_p/v_p [P][Hkv][D], q_r [T_R][Hq][D], k_r/v_r [T_R][Hkv][D]
  * out: o_r [T_R][Hq][D], lse_r [Hq][T_R].
- * Workspace: the two partial states (2 * T_R*Hq*(D+1) floats). */
+ * Workspace: the two partial states (2 * T_R*Hq*(D+1) floats) and transposed V copies. */
 augtree_status augtree_replay_fwd(const augtree_dims *dims, const void *k_p, const void *v_p,
                                   const void *q_r, const void *k_r, const void *v_r, void *o_r,
                                   float *lse_r, void *ws, size_t ws_bytes, void *stream);
@@ -109,7 +117,8 @@ augtree_status augtree_replay_fwd(const augtree_dims *dims, const void *k_p, con
  * out: dq_r [T_R][Hq][D], dk_r/dv_r [T_R][Hkv][D] (own-branch contributions; complete),
  *      dk_p_acc/dv_p_acc [P][Hkv][D] float32: the sum over all branches and all query
  *      heads of each group of the prompt K/V gradient (overwritten, not accumulated into).
- * Workspace: row statistics and, for long prompts, split partial sums. */
+ * Workspace: row statistics, transposed Q/dO/K copies and, when the prompt has few key
+ * tiles, split partial sums. */
 augtree_status augtree_replay_bwd(const augtree_dims *dims, const void *k_p, const void *v_p,
                                   const void *q_r, const void *k_r, const void *v_r,
                                   const void *o_r, const float *lse_r, const void *do_r,
@@ -124,7 +133,7 @@ augtree_status augtree_replay_bwd(const augtree_dims *dims, const void *k_p, con
  *      attention backward)
  * out: dq_p [P][Hq][D], dk_p/dv_p [P][Hkv][D] = prompt queries' contribution + acc,
  *      rounded once to dtype.
- * Workspace: row statistics (Hq*P floats). */
+ * Workspace: row statistics (Hq*P floats) and transposed Q/dO/K copies. */
 augtree_status augtree_prefill_bwd(const augtree_dims *dims, const void *q_p, const void *k_p,
                                    const void *v_p, const void *o_p, const float *lse_p,
                                    const void *do_p, const float *dk_p_acc,
@@ -139,6 +148,7 @@ augtree_status augtree_prefill_bwd(const augtree_dims *dims, const void *q_p, co
  *   prefill_bwd = row_dot(P rows) + prefill_kv_bwd + prefill_dq
  * A prompt key range [key_begin, key_end) lets one call act as one stationary prompt-K/V
  * shard of §3.3 MoveQ: the shard's partial states are later merged per query row.
+ * Each step with a workspace takes the size of its own AUGTREE_OP_* code.
  * Partial states are (normalised output, LSE) pairs: o_part [T_R][Hq][D] float32 and
  * lse_part [Hq][T_R]; a row with no visible key in the range has lse = -inf and o = 0.
  * rowdot [Hq][rows] float32 is sum_d dO[r][h][d] * O[r][h][d] of the saved outputs.
@@ -146,17 +156,19 @@ augtree_status augtree_prefill_bwd(const augtree_dims *dims, const void *q_p, co
 
 /* Partial state of every branch row over prompt keys [key_begin, key_end), no mask
  * (§3.3 MoveQ: a stationary prompt K/V shard evaluates all branch queries).
- * 0 <= key_begin < key_end <= P. */
+ * 0 <= key_begin < key_end <= P. Workspace: AUGTREE_OP_REPLAY_PROMPT_FWD. */
 augtree_status augtree_replay_prompt_fwd(const augtree_dims *dims, const void *k_p,
                                          const void *v_p, const void *q_r, int32_t key_begin,
                                          int32_t key_end, float *o_part, float *lse_part,
-                                         void *stream);
+                                         void *ws, size_t ws_bytes, void *stream);
 
 /* Partial state of every branch row over its own branch, causally (§3.2, Eq. 1: a branch
- * token sees its own earlier tokens and itself, never a sibling). */
+ * token sees its own earlier tokens and itself, never a sibling).
+ * Workspace: AUGTREE_OP_REPLAY_LOCAL_FWD. */
 augtree_status augtree_replay_local_fwd(const augtree_dims *dims, const void *q_r,
                                         const void *k_r, const void *v_r, float *o_part,
-                                        float *lse_part, void *stream);
+                                        float *lse_part, void *ws, size_t ws_bytes,
+                                        void *stream);
 
 /* Exact merge of num_parts (1..AUGTREE_MAX_PARTS) partial states per branch row (§3.3,
  * Fig. 8: states along a query row are combined by the log-sum-exp rule, not by
@@ -183,30 +195,35 @@ augtree_status augtree_replay_prompt_bwd(const augtree_dims *dims, const void *k
                                          float *dv_p_acc, void *ws, size_t ws_bytes,
                                          void *stream);
 
-/* dK/dV of the branch keys (own-branch rows only, causal): dk_r/dv_r [T_R][Hkv][D]. */
+/* dK/dV of the branch keys (own-branch rows only, causal): dk_r/dv_r [T_R][Hkv][D].
+ * Workspace: AUGTREE_OP_REPLAY_LOCAL_BWD. */
 augtree_status augtree_replay_local_bwd(const augtree_dims *dims, const void *q_r,
                                         const void *k_r, const void *v_r, const float *lse_r,
                                         const float *rowdot_r, const void *do_r, void *dk_r,
-                                        void *dv_r, void *stream);
+                                        void *dv_r, void *ws, size_t ws_bytes, void *stream);
 
-/* dQ of every branch row over the whole prompt and its own branch: dq_r [T_R][Hq][D]. */
+/* dQ of every branch row over the whole prompt and its own branch: dq_r [T_R][Hq][D].
+ * Workspace: AUGTREE_OP_REPLAY_DQ. */
 augtree_status augtree_replay_dq(const augtree_dims *dims, const void *k_p, const void *v_p,
                                  const void *q_r, const void *k_r, const void *v_r,
                                  const float *lse_r, const float *rowdot_r, const void *do_r,
-                                 void *dq_r, void *stream);
+                                 void *dq_r, void *ws, size_t ws_bytes, void *stream);
 
 /* Prompt dK/dV: the prompt queries' causal contribution plus dk_p_acc/dv_p_acc (or
- * nothing when both are NULL), rounded once: dk_p/dv_p [P][Hkv][D] (dtype). */
+ * nothing when both are NULL), rounded once: dk_p/dv_p [P][Hkv][D] (dtype).
+ * Workspace: AUGTREE_OP_PREFILL_KV_BWD. */
 augtree_status augtree_prefill_kv_bwd(const augtree_dims *dims, const void *q_p,
                                       const void *k_p, const void *v_p, const float *lse_p,
                                       const float *rowdot_p, const void *do_p,
                                       const float *dk_p_acc, const float *dv_p_acc, void *dk_p,
-                                      void *dv_p, void *stream);
+                                      void *dv_p, void *ws, size_t ws_bytes, void *stream);
 
-/* dQ of the prompt rows (causal over the prompt): dq_p [P][Hq][D]. */
+/* dQ of the prompt rows (causal over the prompt): dq_p [P][Hq][D].
+ * Workspace: AUGTREE_OP_PREFILL_DQ. */
 augtree_status augtree_prefill_dq(const augtree_dims *dims, const void *q_p, const void *k_p,
                                   const void *v_p, const float *lse_p, const float *rowdot_p,
-                                  const void *do_p, void *dq_p, void *stream);
+                                  const void *do_p, void *dq_p, void *ws, size_t ws_bytes,
+                                  void *stream);
 
 /* Bytes of workspace operation `op` (AUGTREE_OP_*) needs for `dims`; 0 for invalid dims. */
 size_t augtree_workspace_bytes(const augtree_dims *dims, int op);

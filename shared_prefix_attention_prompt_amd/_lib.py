@@ -24,6 +24,12 @@ AUGTREE_OP_REPLAY_FWD = 1
 AUGTREE_OP_REPLAY_BWD = 2
 AUGTREE_OP_PREFILL_BWD = 3
 AUGTREE_OP_REPLAY_PROMPT_BWD = 4
+AUGTREE_OP_REPLAY_PROMPT_FWD = 5
+AUGTREE_OP_REPLAY_LOCAL_FWD = 6
+AUGTREE_OP_REPLAY_LOCAL_BWD = 7
+AUGTREE_OP_REPLAY_DQ = 8
+AUGTREE_OP_PREFILL_KV_BWD = 9
+AUGTREE_OP_PREFILL_DQ = 10
 AUGTREE_MAX_BRANCHES = 128
 AUGTREE_MAX_PARTS = 8
 
@@ -70,15 +76,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.augtree_prefill_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     i32 = ctypes.c_int32
     fpp = ctypes.POINTER(ctypes.c_void_p)
-    lib.augtree_replay_prompt_fwd.argtypes = [P, vp, vp, vp, i32, i32, vp, vp, vp]
-    lib.augtree_replay_local_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.augtree_replay_prompt_fwd.argtypes = [P, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+    lib.augtree_replay_local_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.augtree_merge_partials.argtypes = [P, i32, fpp, fpp, vp, vp, vp]
     lib.augtree_row_dot.argtypes = [P, i32, vp, vp, vp, vp]
     lib.augtree_replay_prompt_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
-    lib.augtree_replay_local_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    lib.augtree_replay_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    lib.augtree_prefill_kv_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    lib.augtree_prefill_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.augtree_replay_local_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.augtree_replay_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.augtree_prefill_kv_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.augtree_prefill_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for name in ENTRY_POINTS[:13]:
         getattr(lib, name).restype = st
     lib.augtree_workspace_bytes.argtypes = [P, ctypes.c_int]
@@ -144,13 +150,15 @@ def augtree_prefill_bwd(dims, q_p, k_p, v_p, o_p, lse_p, do_p, dk_p_acc, dv_p_ac
                                       dv_p_acc, dq_p, dk_p, dv_p, ws, ws_bytes, stream)
 
 
-def augtree_replay_prompt_fwd(dims, k_p, v_p, q_r, key_begin, key_end, o_part, lse_part, stream) -> int:
+def augtree_replay_prompt_fwd(dims, k_p, v_p, q_r, key_begin, key_end, o_part, lse_part, ws, ws_bytes,
+                              stream) -> int:
     return load().augtree_replay_prompt_fwd(ctypes.byref(dims), k_p, v_p, q_r, int(key_begin), int(key_end),
-                                            o_part, lse_part, stream)
+                                            o_part, lse_part, ws, ws_bytes, stream)
 
 
-def augtree_replay_local_fwd(dims, q_r, k_r, v_r, o_part, lse_part, stream) -> int:
-    return load().augtree_replay_local_fwd(ctypes.byref(dims), q_r, k_r, v_r, o_part, lse_part, stream)
+def augtree_replay_local_fwd(dims, q_r, k_r, v_r, o_part, lse_part, ws, ws_bytes, stream) -> int:
+    return load().augtree_replay_local_fwd(ctypes.byref(dims), q_r, k_r, v_r, o_part, lse_part, ws, ws_bytes,
+                                           stream)
 
 
 def augtree_merge_partials(dims, o_parts, lse_parts, o_r, lse_r, stream) -> int:
@@ -171,21 +179,23 @@ def augtree_replay_prompt_bwd(dims, k_p, v_p, q_r, lse_r, rowdot_r, do_r, key_be
                                             stream)
 
 
-def augtree_replay_local_bwd(dims, q_r, k_r, v_r, lse_r, rowdot_r, do_r, dk_r, dv_r, stream) -> int:
+def augtree_replay_local_bwd(dims, q_r, k_r, v_r, lse_r, rowdot_r, do_r, dk_r, dv_r, ws, ws_bytes,
+                             stream) -> int:
     return load().augtree_replay_local_bwd(ctypes.byref(dims), q_r, k_r, v_r, lse_r, rowdot_r, do_r, dk_r,
-                                           dv_r, stream)
+                                           dv_r, ws, ws_bytes, stream)
 
 
-def augtree_replay_dq(dims, k_p, v_p, q_r, k_r, v_r, lse_r, rowdot_r, do_r, dq_r, stream) -> int:
+def augtree_replay_dq(dims, k_p, v_p, q_r, k_r, v_r, lse_r, rowdot_r, do_r, dq_r, ws, ws_bytes, stream) -> int:
     return load().augtree_replay_dq(ctypes.byref(dims), k_p, v_p, q_r, k_r, v_r, lse_r, rowdot_r, do_r, dq_r,
-                                    stream)
+                                    ws, ws_bytes, stream)
 
 
 def augtree_prefill_kv_bwd(dims, q_p, k_p, v_p, lse_p, rowdot_p, do_p, dk_p_acc, dv_p_acc, dk_p, dv_p,
-                           stream) -> int:
+                           ws, ws_bytes, stream) -> int:
     return load().augtree_prefill_kv_bwd(ctypes.byref(dims), q_p, k_p, v_p, lse_p, rowdot_p, do_p, dk_p_acc,
-                                         dv_p_acc, dk_p, dv_p, stream)
+                                         dv_p_acc, dk_p, dv_p, ws, ws_bytes, stream)
 
 
-def augtree_prefill_dq(dims, q_p, k_p, v_p, lse_p, rowdot_p, do_p, dq_p, stream) -> int:
-    return load().augtree_prefill_dq(ctypes.byref(dims), q_p, k_p, v_p, lse_p, rowdot_p, do_p, dq_p, stream)
+def augtree_prefill_dq(dims, q_p, k_p, v_p, lse_p, rowdot_p, do_p, dq_p, ws, ws_bytes, stream) -> int:
+    return load().augtree_prefill_dq(ctypes.byref(dims), q_p, k_p, v_p, lse_p, rowdot_p, do_p, dq_p, ws,
+                                     ws_bytes, stream)

@@ -1,13 +1,12 @@
 // Host side of the C ABI declared in include/augtree.h: argument validation, workspace
-// layout, branch tables and the launch sequence of each entry point. Nothing here
-// allocates, frees or synchronises; all work goes to the caller's stream.
+// layout, branch tables, transposed operand copies and the launch sequence of each entry
+// point. Nothing here allocates, frees or synchronises; all work goes to the caller's stream.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
 #include <string>
-#include <vector>
 
 #include "../../include/augtree.h"
 #include "kernels.hpp"
@@ -32,7 +31,12 @@ struct Shape {
   int P = 0, G = 0, Hq = 0, Hkv = 0, D = 0, dtype = 0, T = 0;
   float scale = 0.f;
   int off[kMaxBranches + 1] = {};
+  int pad[kMaxBranches + 1] = {};  // branch column offsets in transposed copies
+  size_t esz() const { return dtype == AUGTREE_BF16 ? 2 : 4; }
+  int Tp() const { return pad[G]; }  // padded columns of a response transposed copy
 };
+
+int pad64(int n) { return (n + kSeg - 1) / kSeg * kSeg; }
 
 augtree_status check_dims(const augtree_dims* d, Shape* s) {
   if (d == nullptr) return fail(AUGTREE_ERR_INVALID_ARGUMENT, "dims is NULL");
@@ -63,6 +67,11 @@ augtree_status check_dims(const augtree_dims* d, Shape* s) {
     return fail(AUGTREE_ERR_UNSUPPORTED, "bf16 head_dim %d not built (64 or 128)", d->head_dim);
   if (d->dtype == AUGTREE_F32 && d->head_dim != 64)
     return fail(AUGTREE_ERR_UNSUPPORTED, "f32 head_dim %d not built (64)", d->head_dim);
+  // every index of the kernels (elements of one tensor, rows x heads) stays in 32 bits
+  const int64_t T = d->branch_offsets[d->num_branches];
+  const int64_t rows = T > d->prompt_len ? T : d->prompt_len;
+  if ((rows + (int64_t)kSeg * d->num_branches) * d->num_q_heads * d->head_dim > INT32_MAX)
+    return fail(AUGTREE_ERR_UNSUPPORTED, "rows x heads x head_dim beyond 2^31 elements");
   s->P = d->prompt_len;
   s->G = d->num_branches;
   s->Hq = d->num_q_heads;
@@ -70,7 +79,9 @@ augtree_status check_dims(const augtree_dims* d, Shape* s) {
   s->D = d->head_dim;
   s->dtype = d->dtype;
   s->scale = d->softmax_scale;
+  s->pad[0] = 0;
   for (int i = 0; i <= s->G; ++i) s->off[i] = d->branch_offsets[i];
+  for (int i = 0; i < s->G; ++i) s->pad[i + 1] = s->pad[i] + pad64(s->off[i + 1] - s->off[i]);
   s->T = s->off[s->G];
   return AUGTREE_OK;
 }
@@ -100,14 +111,21 @@ augtree_status check_ptr(const void* p, const char* name, bool may_be_null = fal
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// ---- workspace pieces ----
+// Transposed copies: [H][D][cols] of dtype.
+size_t tr_bytes(const Shape& s, int H, int cols) { return align_up((size_t)H * s.D * cols * s.esz()); }
+size_t tr_prompt(const Shape& s, int H) { return tr_bytes(s, H, pad64(s.P)); }
+size_t tr_resp(const Shape& s, int H) { return tr_bytes(s, H, s.Tp()); }
+
 // Split count of the prompt dK/dV pass over the branches' rows for `nkeys` prompt keys:
-// enough workgroups to give every compute unit about two, never more parts than query
-// tiles, at most 16.
+// enough workgroups (one per compute unit at a time) for about two rounds on 256 compute
+// units, never more parts than query tiles, at most 16.
 int prompt_split(const Shape& s, int nkeys) {
-  const int64_t wgs = (int64_t)((nkeys + kDkdvBN - 1) / kDkdvBN) * s.Hkv;
+  const int64_t wgs = (int64_t)((nkeys + kDkdvKeysPerWG - 1) / kDkdvKeysPerWG) * s.Hkv;
   const int64_t target = 512;
   int64_t n = (target + wgs - 1) / wgs;
-  const int64_t qtiles = (s.T + kDkdvBM - 1) / kDkdvBM;
+  int64_t qtiles = 0;
+  for (int i = 0; i < s.G; ++i) qtiles += (s.off[i + 1] - s.off[i] + kDkdvBM - 1) / kDkdvBM;
   if (n > qtiles) n = qtiles;
   if (n > 16) n = 16;
   if (n < 1) n = 1;
@@ -120,14 +138,13 @@ size_t prompt_split_floats(const Shape& s, int nkeys) {
   return n > 1 ? (size_t)n * nkeys * s.Hkv * s.D : 0;
 }
 
-// Workspace of augtree_replay_prompt_bwd: sized for the largest key range a call may use
-// (any range needs at most what some range of whole tiles needs; the maximum is taken
-// over the tile counts, which is cheap for any realistic prompt).
-size_t prompt_bwd_ws(const Shape& s) {
+// Split partials of augtree_replay_prompt_bwd: sized for the largest key range a call may use
+// (the maximum over whole-tile ranges, which bounds every range).
+size_t prompt_split_ws(const Shape& s) {
   size_t best = 0;
-  const int nkt = (s.P + kDkdvBN - 1) / kDkdvBN;
+  const int nkt = (s.P + kDkdvKeysPerWG - 1) / kDkdvKeysPerWG;
   for (int t = 1; t <= nkt; ++t) {
-    const int nk = t == nkt ? s.P : t * kDkdvBN;
+    const int nk = t == nkt ? s.P : t * kDkdvKeysPerWG;
     const size_t f = prompt_split_floats(s, nk);
     if (f > best) best = f;
     if (prompt_split(s, nk) == 1) break;  // larger ranges do not split
@@ -135,30 +152,72 @@ size_t prompt_bwd_ws(const Shape& s) {
   return align_up(2 * best * sizeof(float));
 }
 
-struct ReplayFwdWs { size_t o_a, o_b, lse_a, lse_b, total; };
+// Layout of a workspace as consecutive 256-byte aligned pieces.
+struct Layout {
+  size_t total = 0;
+  size_t add(size_t bytes) {
+    const size_t at = total;
+    total += align_up(bytes);
+    return at;
+  }
+};
+
+struct ReplayFwdWs { size_t o_a, o_b, lse_a, lse_b, vpt, vrt, total; };
 ReplayFwdWs replay_fwd_ws(const Shape& s) {
   ReplayFwdWs w;
-  const size_t o = align_up((size_t)s.T * s.Hq * s.D * sizeof(float));
-  const size_t l = align_up((size_t)s.T * s.Hq * sizeof(float));
-  w.o_a = 0;
-  w.o_b = o;
-  w.lse_a = 2 * o;
-  w.lse_b = 2 * o + l;
-  w.total = 2 * o + 2 * l;
+  Layout l;
+  w.o_a = l.add((size_t)s.T * s.Hq * s.D * sizeof(float));
+  w.o_b = l.add((size_t)s.T * s.Hq * s.D * sizeof(float));
+  w.lse_a = l.add((size_t)s.T * s.Hq * sizeof(float));
+  w.lse_b = l.add((size_t)s.T * s.Hq * sizeof(float));
+  w.vpt = l.add(tr_prompt(s, s.Hkv));
+  w.vrt = l.add(tr_resp(s, s.Hkv));
+  w.total = l.total;
   return w;
 }
 
-struct ReplayBwdWs { size_t rowdot, prompt, total; };
+struct ReplayBwdWs { size_t rowdot, qrt, dort, kpt, krt, split, total; };
 ReplayBwdWs replay_bwd_ws(const Shape& s) {
   ReplayBwdWs w;
-  const size_t rd = align_up((size_t)s.T * s.Hq * sizeof(float));
-  w.rowdot = 0;
-  w.prompt = rd;
-  w.total = rd + prompt_bwd_ws(s);
+  Layout l;
+  w.rowdot = l.add((size_t)s.T * s.Hq * sizeof(float));
+  w.qrt = l.add(tr_resp(s, s.Hq));
+  w.dort = l.add(tr_resp(s, s.Hq));
+  w.kpt = l.add(tr_prompt(s, s.Hkv));
+  w.krt = l.add(tr_resp(s, s.Hkv));
+  w.split = l.add(prompt_split_ws(s));
+  w.total = l.total;
   return w;
 }
 
-size_t prefill_bwd_ws(const Shape& s) { return align_up((size_t)s.P * s.Hq * sizeof(float)); }
+struct PrefillBwdWs { size_t rowdot, qpt, dopt, kpt, total; };
+PrefillBwdWs prefill_bwd_ws(const Shape& s) {
+  PrefillBwdWs w;
+  Layout l;
+  w.rowdot = l.add((size_t)s.P * s.Hq * sizeof(float));
+  w.qpt = l.add(tr_prompt(s, s.Hq));
+  w.dopt = l.add(tr_prompt(s, s.Hq));
+  w.kpt = l.add(tr_prompt(s, s.Hkv));
+  w.total = l.total;
+  return w;
+}
+
+size_t op_workspace(const Shape& s, int op) {
+  switch (op) {
+    case AUGTREE_OP_PREFILL_FWD: return tr_prompt(s, s.Hkv);
+    case AUGTREE_OP_REPLAY_FWD: return replay_fwd_ws(s).total;
+    case AUGTREE_OP_REPLAY_BWD: return replay_bwd_ws(s).total;
+    case AUGTREE_OP_PREFILL_BWD: return prefill_bwd_ws(s).total;
+    case AUGTREE_OP_REPLAY_PROMPT_BWD: return 2 * tr_resp(s, s.Hq) + prompt_split_ws(s);
+    case AUGTREE_OP_REPLAY_PROMPT_FWD: return tr_prompt(s, s.Hkv);
+    case AUGTREE_OP_REPLAY_LOCAL_FWD: return tr_resp(s, s.Hkv);
+    case AUGTREE_OP_REPLAY_LOCAL_BWD: return 2 * tr_resp(s, s.Hq);
+    case AUGTREE_OP_REPLAY_DQ: return tr_prompt(s, s.Hkv) + tr_resp(s, s.Hkv);
+    case AUGTREE_OP_PREFILL_KV_BWD: return 2 * tr_prompt(s, s.Hq);
+    case AUGTREE_OP_PREFILL_DQ: return tr_prompt(s, s.Hkv);
+  }
+  return 0;
+}
 
 augtree_status check_ws(const void* ws, size_t have, size_t need) {
   if (need == 0) return AUGTREE_OK;
@@ -169,7 +228,7 @@ augtree_status check_ws(const void* ws, size_t have, size_t need) {
   return AUGTREE_OK;
 }
 
-// Table of the branches for kernels that tile each branch separately.
+// Table of the branches; tile_prefix counts tiles of `tile` rows per branch.
 BranchTable branch_table(const Shape& s, int tile) {
   BranchTable bt;
   memset(&bt, 0, sizeof(bt));
@@ -177,6 +236,7 @@ BranchTable branch_table(const Shape& s, int tile) {
   int acc = 0;
   for (int i = 0; i <= s.G; ++i) {
     bt.off[i] = s.off[i];
+    bt.pad[i] = s.pad[i];
     bt.tile_prefix[i] = acc;
     if (i < s.G) acc += (s.off[i + 1] - s.off[i] + tile - 1) / tile;
   }
@@ -187,49 +247,96 @@ int total_tiles(const BranchTable& bt) { return bt.tile_prefix[bt.G]; }
 
 char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
+// ---- transposed copies ----
+// rows [r0, r0 + n) of x [rows][H][D] (one segment) -> [H][D][pad64(n)].
+augtree_status transpose_range(const Shape& s, const void* x, int H, int r0, int n, void* dst, hipStream_t st) {
+  TransposeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.src = static_cast<const char*>(x) + (size_t)r0 * H * s.D * s.esz();
+  a.dst = dst;
+  a.H = H;
+  a.cols = pad64(n);
+  a.nseg = 1;
+  a.seg.G = 1;
+  a.seg.off[0] = 0;
+  a.seg.off[1] = n;
+  a.seg.pad[0] = 0;
+  a.seg.pad[1] = a.cols;
+  a.seg.tile_prefix[0] = 0;
+  a.seg.tile_prefix[1] = a.cols / kSeg;
+  LAUNCH(launch_transpose(s.dtype, s.D, a, st), "transposed copy");
+  return AUGTREE_OK;
+}
+
+// all branches of x [T_R][H][D] -> [H][D][Tp], every branch padded to 64 columns.
+augtree_status transpose_branches(const Shape& s, const void* x, int H, void* dst, hipStream_t st) {
+  TransposeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.src = x;
+  a.dst = dst;
+  a.H = H;
+  a.cols = s.Tp();
+  a.nseg = s.G;
+  a.seg.G = s.G;
+  for (int i = 0; i <= s.G; ++i) {
+    a.seg.off[i] = s.off[i];
+    a.seg.pad[i] = s.pad[i];
+    a.seg.tile_prefix[i] = s.pad[i] / kSeg;
+  }
+  LAUNCH(launch_transpose(s.dtype, s.D, a, st), "transposed copy (branches)");
+  return AUGTREE_OK;
+}
+
 // ---------------------------------------------------------------------------------------
-// Single steps on validated shapes (no argument checks here).
+// Single steps on validated shapes (no argument checks here). Transposed copies are passed
+// in, already written.
 // ---------------------------------------------------------------------------------------
-augtree_status step_prefill_fwd(const Shape& s, const void* q_p, const void* k_p, const void* v_p,
-                                void* o_p, float* lse_p, hipStream_t st) {
+int heads_slots(const Shape& s) { return s.Hq / heads_per_wg(s.Hq / s.Hkv); }
+
+augtree_status step_prefill_fwd(const Shape& s, const void* q_p, const void* k_p, const void* vpt, void* o_p,
+                                float* lse_p, hipStream_t st) {
   FwdArgs a;
   memset(&a, 0, sizeof(a));
-  a.q = q_p; a.k = k_p; a.v = v_p; a.o = o_p; a.lse = lse_p;
+  a.q = q_p; a.k = k_p; a.vt = vpt; a.o = o_p; a.lse = lse_p;
   a.Hq = s.Hq; a.Hkv = s.Hkv;
-  a.nq_rows = s.P; a.nkv_rows = s.P;
-  a.ntiles = (s.P + kFwdBM - 1) / kFwdBM;
+  a.nq_rows = s.P; a.nkv_rows = s.P; a.vt_cols = pad64(s.P);
+  const int rt = fwd_rows_per_wg(s.Hq / s.Hkv);
+  a.ntiles = (s.P + rt - 1) / rt;
+  a.nwg = a.ntiles * heads_slots(s);
   a.scale_log2 = s.scale * kLog2e;
   LAUNCH(launch_attn_fwd(s.dtype, s.D, kFwdPrefill, a, st), "prefill forward");
   return AUGTREE_OK;
 }
 
-augtree_status step_replay_prompt_fwd(const Shape& s, const void* k_p, const void* v_p, const void* q_r,
-                                      int kb, int ke, float* o_part, float* lse_part, hipStream_t st) {
-  const size_t esz = s.dtype == AUGTREE_BF16 ? 2 : 4;
-  const size_t koff = (size_t)kb * s.Hkv * s.D * esz;
+// vt: transposed copy of prompt V rows [kb, ke) (pad64(ke - kb) columns)
+augtree_status step_replay_prompt_fwd(const Shape& s, const void* k_p, const void* vt, const void* q_r, int kb,
+                                      int ke, float* o_part, float* lse_part, hipStream_t st) {
   FwdArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q_r;
-  a.k = static_cast<const char*>(k_p) + koff;
-  a.v = static_cast<const char*>(v_p) + koff;
+  a.k = static_cast<const char*>(k_p) + (size_t)kb * s.Hkv * s.D * s.esz();
+  a.vt = vt;
   a.o = o_part; a.lse = lse_part;
   a.Hq = s.Hq; a.Hkv = s.Hkv;
-  a.nq_rows = s.T; a.nkv_rows = ke - kb;
-  a.ntiles = (s.T + kFwdBM - 1) / kFwdBM;
+  a.nq_rows = s.T; a.nkv_rows = ke - kb; a.vt_cols = pad64(ke - kb);
+  const int rt = fwd_rows_per_wg(s.Hq / s.Hkv);
+  a.ntiles = (s.T + rt - 1) / rt;
+  a.nwg = a.ntiles * heads_slots(s);
   a.scale_log2 = s.scale * kLog2e;
   LAUNCH(launch_attn_fwd(s.dtype, s.D, kFwdReplayPrompt, a, st), "replay forward (prompt keys)");
   return AUGTREE_OK;
 }
 
-augtree_status step_replay_local_fwd(const Shape& s, const void* q_r, const void* k_r, const void* v_r,
+augtree_status step_replay_local_fwd(const Shape& s, const void* q_r, const void* k_r, const void* vrt,
                                      float* o_part, float* lse_part, hipStream_t st) {
   FwdArgs b;
   memset(&b, 0, sizeof(b));
-  b.q = q_r; b.k = k_r; b.v = v_r; b.o = o_part; b.lse = lse_part;
+  b.q = q_r; b.k = k_r; b.vt = vrt; b.o = o_part; b.lse = lse_part;
   b.Hq = s.Hq; b.Hkv = s.Hkv;
-  b.nq_rows = s.T; b.nkv_rows = s.T;
-  b.bt = branch_table(s, kFwdBM);
+  b.nq_rows = s.T; b.nkv_rows = s.T; b.vt_cols = s.Tp();
+  b.bt = branch_table(s, fwd_rows_per_wg(s.Hq / s.Hkv));
   b.ntiles = total_tiles(b.bt);
+  b.nwg = b.ntiles * heads_slots(s);
   b.scale_log2 = s.scale * kLog2e;
   LAUNCH(launch_attn_fwd(s.dtype, s.D, kFwdReplayLocal, b, st), "replay forward (branch keys)");
   return AUGTREE_OK;
@@ -257,28 +364,33 @@ augtree_status step_row_dot(const Shape& s, int rows, const void* o, const void*
   return AUGTREE_OK;
 }
 
+// qrt/dort: transposed branch copies of q_r / do_r; split: split-partial workspace
 augtree_status step_replay_prompt_bwd(const Shape& s, const void* k_p, const void* v_p, const void* q_r,
-                                      const float* lse_r, const float* rowdot_r, const void* do_r, int kb,
-                                      int ke, float* dk_acc, float* dv_acc, void* ws, hipStream_t st) {
+                                      const void* qrt, const float* lse_r, const float* rowdot_r, const void* do_r,
+                                      const void* dort, int kb, int ke, float* dk_acc, float* dv_acc, void* split,
+                                      hipStream_t st) {
   const int nkeys = ke - kb;
   const int nsplit = prompt_split(s, nkeys);
-  const size_t esz = s.dtype == AUGTREE_BF16 ? 2 : 4;
   const size_t koff = (size_t)kb * s.Hkv * s.D;
   const int64_t part = (int64_t)nkeys * s.Hkv * s.D;
-  float* part_dk = static_cast<float*>(ws);
+  float* part_dk = static_cast<float*>(split);
   float* part_dv = part_dk + (nsplit > 1 ? (int64_t)nsplit * part : 0);
   DkdvArgs p;
   memset(&p, 0, sizeof(p));
-  p.q = q_r; p.dout = do_r; p.lse = lse_r; p.rowdot = rowdot_r;
-  p.k = static_cast<const char*>(k_p) + koff * esz;
-  p.v = static_cast<const char*>(v_p) + koff * esz;
+  p.q = q_r; p.dout = do_r; p.qt = qrt; p.dot = dort; p.lse = lse_r; p.rowdot = rowdot_r;
+  p.k = static_cast<const char*>(k_p) + koff * s.esz();
+  p.v = static_cast<const char*>(v_p) + koff * s.esz();
   p.nsplit = nsplit;
+  p.causal = 0;
   p.dk = nsplit > 1 ? static_cast<void*>(part_dk) : static_cast<void*>(dk_acc + koff);
   p.dv = nsplit > 1 ? static_cast<void*>(part_dv) : static_cast<void*>(dv_acc + koff);
   p.split_stride = part;
   p.Hq = s.Hq; p.Hkv = s.Hkv;
-  p.nq_rows = s.T; p.nkv_rows = nkeys;
-  p.nktiles = (nkeys + kDkdvBN - 1) / kDkdvBN;
+  p.nq_rows = s.T; p.nkv_rows = nkeys; p.qt_cols = s.Tp();
+  p.nktiles = (nkeys + kDkdvKeysPerWG - 1) / kDkdvKeysPerWG;
+  p.bt = branch_table(s, kDkdvBM);
+  p.nqtiles = total_tiles(p.bt);
+  p.nwg = p.nktiles * s.Hkv * nsplit;
   p.scale = s.scale; p.scale_log2 = s.scale * kLog2e;
   LAUNCH(launch_dkdv(s.dtype, s.D, kDkdvPromptFromReplay, p, st), "prompt dK/dV from branches");
   if (nsplit > 1) {
@@ -287,75 +399,84 @@ augtree_status step_replay_prompt_bwd(const Shape& s, const void* k_p, const voi
     sr.nsplit = nsplit;
     sr.part = part_dk;
     sr.out = dk_acc + koff;
-    LAUNCH(launch_split_reduce(sr, 1, st), "split reduce (dK)");
+    LAUNCH(launch_split_reduce(sr, st), "split reduce (dK)");
     sr.part = part_dv;
     sr.out = dv_acc + koff;
-    LAUNCH(launch_split_reduce(sr, 1, st), "split reduce (dV)");
+    LAUNCH(launch_split_reduce(sr, st), "split reduce (dV)");
   }
   return AUGTREE_OK;
 }
 
-augtree_status step_replay_local_bwd(const Shape& s, const void* q_r, const void* k_r, const void* v_r,
-                                     const float* lse_r, const float* rowdot_r, const void* do_r, void* dk_r,
-                                     void* dv_r, hipStream_t st) {
+augtree_status step_replay_local_bwd(const Shape& s, const void* q_r, const void* qrt, const void* k_r,
+                                     const void* v_r, const float* lse_r, const float* rowdot_r, const void* do_r,
+                                     const void* dort, void* dk_r, void* dv_r, hipStream_t st) {
   DkdvArgs l;
   memset(&l, 0, sizeof(l));
-  l.q = q_r; l.dout = do_r; l.lse = lse_r; l.rowdot = rowdot_r;
+  l.q = q_r; l.dout = do_r; l.qt = qrt; l.dot = dort; l.lse = lse_r; l.rowdot = rowdot_r;
   l.k = k_r; l.v = v_r; l.dk = dk_r; l.dv = dv_r;
   l.Hq = s.Hq; l.Hkv = s.Hkv;
-  l.nq_rows = s.T; l.nkv_rows = s.T;
-  l.bt = branch_table(s, kDkdvBN);
+  l.nq_rows = s.T; l.nkv_rows = s.T; l.qt_cols = s.Tp();
+  l.bt = branch_table(s, kDkdvKeysPerWG);
   l.nktiles = total_tiles(l.bt);
   l.nsplit = 1;
+  l.causal = 1;
+  l.nwg = l.nktiles * s.Hkv;
   l.scale = s.scale; l.scale_log2 = s.scale * kLog2e;
   LAUNCH(launch_dkdv(s.dtype, s.D, kDkdvLocal, l, st), "branch dK/dV");
   return AUGTREE_OK;
 }
 
-augtree_status step_replay_dq(const Shape& s, const void* k_p, const void* v_p, const void* q_r,
-                              const void* k_r, const void* v_r, const float* lse_r, const float* rowdot_r,
-                              const void* do_r, void* dq_r, hipStream_t st) {
+augtree_status step_replay_dq(const Shape& s, const void* k_p, const void* kpt, const void* v_p, const void* q_r,
+                              const void* k_r, const void* krt, const void* v_r, const float* lse_r,
+                              const float* rowdot_r, const void* do_r, void* dq_r, hipStream_t st) {
   DqArgs q;
   memset(&q, 0, sizeof(q));
   q.q = q_r; q.dout = do_r; q.lse = lse_r; q.rowdot = rowdot_r;
-  q.k = k_r; q.v = v_r; q.kp = k_p; q.vp = v_p; q.dq = dq_r;
+  q.k = k_r; q.v = v_r; q.kt = krt; q.kp = k_p; q.vp = v_p; q.kpt = kpt; q.dq = dq_r;
   q.Hq = s.Hq; q.Hkv = s.Hkv;
   q.nq_rows = s.T; q.nkv_rows = s.T; q.nprompt = s.P;
-  q.bt = branch_table(s, kDqBM);
+  q.kt_cols = s.Tp(); q.kpt_cols = pad64(s.P);
+  q.bt = branch_table(s, 32 * 8 / heads_per_wg(s.Hq / s.Hkv));
   q.ntiles = total_tiles(q.bt);
+  q.nwg = q.ntiles * heads_slots(s);
   q.scale = s.scale; q.scale_log2 = s.scale * kLog2e;
   LAUNCH(launch_dq(s.dtype, s.D, kDqResponse, q, st), "branch dQ");
   return AUGTREE_OK;
 }
 
-augtree_status step_prefill_kv_bwd(const Shape& s, const void* q_p, const void* k_p, const void* v_p,
-                                   const float* lse_p, const float* rowdot_p, const void* do_p,
-                                   const float* dk_acc, const float* dv_acc, void* dk_p, void* dv_p,
-                                   hipStream_t st) {
+augtree_status step_prefill_kv_bwd(const Shape& s, const void* q_p, const void* qpt, const void* k_p,
+                                   const void* v_p, const float* lse_p, const float* rowdot_p, const void* do_p,
+                                   const void* dopt, const float* dk_acc, const float* dv_acc, void* dk_p,
+                                   void* dv_p, hipStream_t st) {
   DkdvArgs p;
   memset(&p, 0, sizeof(p));
-  p.q = q_p; p.dout = do_p; p.lse = lse_p; p.rowdot = rowdot_p;
+  p.q = q_p; p.dout = do_p; p.qt = qpt; p.dot = dopt; p.lse = lse_p; p.rowdot = rowdot_p;
   p.k = k_p; p.v = v_p; p.dk = dk_p; p.dv = dv_p;
   p.init_dk = dk_acc; p.init_dv = dv_acc;
   p.Hq = s.Hq; p.Hkv = s.Hkv;
-  p.nq_rows = s.P; p.nkv_rows = s.P;
-  p.nktiles = (s.P + kDkdvBN - 1) / kDkdvBN;
+  p.nq_rows = s.P; p.nkv_rows = s.P; p.qt_cols = pad64(s.P);
+  p.nktiles = (s.P + kDkdvKeysPerWG - 1) / kDkdvKeysPerWG;
   p.nsplit = 1;
+  p.causal = 1;
+  p.nwg = p.nktiles * s.Hkv;
   p.scale = s.scale; p.scale_log2 = s.scale * kLog2e;
   LAUNCH(launch_dkdv(s.dtype, s.D, kDkdvPrefill, p, st), "prefill dK/dV");
   return AUGTREE_OK;
 }
 
-augtree_status step_prefill_dq(const Shape& s, const void* q_p, const void* k_p, const void* v_p,
+augtree_status step_prefill_dq(const Shape& s, const void* q_p, const void* k_p, const void* kpt, const void* v_p,
                                const float* lse_p, const float* rowdot_p, const void* do_p, void* dq_p,
                                hipStream_t st) {
   DqArgs q;
   memset(&q, 0, sizeof(q));
   q.q = q_p; q.dout = do_p; q.lse = lse_p; q.rowdot = rowdot_p;
-  q.k = k_p; q.v = v_p; q.dq = dq_p;
+  q.k = k_p; q.v = v_p; q.kt = kpt; q.dq = dq_p;
   q.Hq = s.Hq; q.Hkv = s.Hkv;
   q.nq_rows = s.P; q.nkv_rows = s.P; q.nprompt = 0;
-  q.ntiles = (s.P + kDqBM - 1) / kDqBM;
+  q.kt_cols = pad64(s.P);
+  const int rt = 32 * 8 / heads_per_wg(s.Hq / s.Hkv);
+  q.ntiles = (s.P + rt - 1) / rt;
+  q.nwg = q.ntiles * heads_slots(s);
   q.scale = s.scale; q.scale_log2 = s.scale * kLog2e;
   LAUNCH(launch_dq(s.dtype, s.D, kDqPrefill, q, st), "prefill dQ");
   return AUGTREE_OK;
@@ -399,35 +520,34 @@ size_t augtree_workspace_bytes(const augtree_dims* dims, int op) {
     t_last_error = saved;
     return 0;
   }
-  switch (op) {
-    case AUGTREE_OP_PREFILL_FWD: return 0;
-    case AUGTREE_OP_REPLAY_FWD: return replay_fwd_ws(s).total;
-    case AUGTREE_OP_REPLAY_BWD: return replay_bwd_ws(s).total;
-    case AUGTREE_OP_PREFILL_BWD: return prefill_bwd_ws(s);
-    case AUGTREE_OP_REPLAY_PROMPT_BWD: return prompt_bwd_ws(s);
-  }
-  return 0;
+  return op_workspace(s, op);
 }
 
 // ---- single steps ----
 
 augtree_status augtree_replay_prompt_fwd(const augtree_dims* dims, const void* k_p, const void* v_p,
                                          const void* q_r, int32_t key_begin, int32_t key_end, float* o_part,
-                                         float* lse_part, void* stream) {
+                                         float* lse_part, void* ws, size_t ws_bytes, void* stream) {
   Shape s;
   CHECK(check_dims(dims, &s));
   CHECK(check_key_range(s, key_begin, key_end));
   PTR(k_p); PTR(v_p); PTR(q_r); PTR(o_part); PTR(lse_part);
-  return step_replay_prompt_fwd(s, k_p, v_p, q_r, key_begin, key_end, o_part, lse_part,
-                                static_cast<hipStream_t>(stream));
+  CHECK(check_ws(ws, ws_bytes, op_workspace(s, AUGTREE_OP_REPLAY_PROMPT_FWD)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  CHECK(transpose_range(s, v_p, s.Hkv, key_begin, key_end - key_begin, ws, st));
+  return step_replay_prompt_fwd(s, k_p, ws, q_r, key_begin, key_end, o_part, lse_part, st);
 }
 
 augtree_status augtree_replay_local_fwd(const augtree_dims* dims, const void* q_r, const void* k_r,
-                                        const void* v_r, float* o_part, float* lse_part, void* stream) {
+                                        const void* v_r, float* o_part, float* lse_part, void* ws,
+                                        size_t ws_bytes, void* stream) {
   Shape s;
   CHECK(check_dims(dims, &s));
   PTR(q_r); PTR(k_r); PTR(v_r); PTR(o_part); PTR(lse_part);
-  return step_replay_local_fwd(s, q_r, k_r, v_r, o_part, lse_part, static_cast<hipStream_t>(stream));
+  CHECK(check_ws(ws, ws_bytes, op_workspace(s, AUGTREE_OP_REPLAY_LOCAL_FWD)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  CHECK(transpose_branches(s, v_r, s.Hkv, ws, st));
+  return step_replay_local_fwd(s, q_r, k_r, ws, o_part, lse_part, st);
 }
 
 augtree_status augtree_merge_partials(const augtree_dims* dims, int32_t num_parts, const float* const* o_parts,
@@ -464,35 +584,52 @@ augtree_status augtree_replay_prompt_bwd(const augtree_dims* dims, const void* k
   CHECK(check_dims(dims, &s));
   CHECK(check_key_range(s, key_begin, key_end));
   PTR(k_p); PTR(v_p); PTR(q_r); PTR(lse_r); PTR(rowdot_r); PTR(do_r); PTR(dk_p_acc); PTR(dv_p_acc);
-  CHECK(check_ws(ws, ws_bytes, prompt_bwd_ws(s)));
-  return step_replay_prompt_bwd(s, k_p, v_p, q_r, lse_r, rowdot_r, do_r, key_begin, key_end, dk_p_acc,
-                                dv_p_acc, ws, static_cast<hipStream_t>(stream));
+  CHECK(check_ws(ws, ws_bytes, op_workspace(s, AUGTREE_OP_REPLAY_PROMPT_BWD)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* qrt = ws;
+  void* dort = at(ws, tr_resp(s, s.Hq));
+  void* split = at(ws, 2 * tr_resp(s, s.Hq));
+  CHECK(transpose_branches(s, q_r, s.Hq, qrt, st));
+  CHECK(transpose_branches(s, do_r, s.Hq, dort, st));
+  return step_replay_prompt_bwd(s, k_p, v_p, q_r, qrt, lse_r, rowdot_r, do_r, dort, key_begin, key_end, dk_p_acc,
+                                dv_p_acc, split, st);
 }
 
 augtree_status augtree_replay_local_bwd(const augtree_dims* dims, const void* q_r, const void* k_r,
                                         const void* v_r, const float* lse_r, const float* rowdot_r,
-                                        const void* do_r, void* dk_r, void* dv_r, void* stream) {
+                                        const void* do_r, void* dk_r, void* dv_r, void* ws, size_t ws_bytes,
+                                        void* stream) {
   Shape s;
   CHECK(check_dims(dims, &s));
   PTR(q_r); PTR(k_r); PTR(v_r); PTR(lse_r); PTR(rowdot_r); PTR(do_r); PTR(dk_r); PTR(dv_r);
-  return step_replay_local_bwd(s, q_r, k_r, v_r, lse_r, rowdot_r, do_r, dk_r, dv_r,
-                               static_cast<hipStream_t>(stream));
+  CHECK(check_ws(ws, ws_bytes, op_workspace(s, AUGTREE_OP_REPLAY_LOCAL_BWD)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* qrt = ws;
+  void* dort = at(ws, tr_resp(s, s.Hq));
+  CHECK(transpose_branches(s, q_r, s.Hq, qrt, st));
+  CHECK(transpose_branches(s, do_r, s.Hq, dort, st));
+  return step_replay_local_bwd(s, q_r, qrt, k_r, v_r, lse_r, rowdot_r, do_r, dort, dk_r, dv_r, st);
 }
 
 augtree_status augtree_replay_dq(const augtree_dims* dims, const void* k_p, const void* v_p, const void* q_r,
                                  const void* k_r, const void* v_r, const float* lse_r, const float* rowdot_r,
-                                 const void* do_r, void* dq_r, void* stream) {
+                                 const void* do_r, void* dq_r, void* ws, size_t ws_bytes, void* stream) {
   Shape s;
   CHECK(check_dims(dims, &s));
   PTR(k_p); PTR(v_p); PTR(q_r); PTR(k_r); PTR(v_r); PTR(lse_r); PTR(rowdot_r); PTR(do_r); PTR(dq_r);
-  return step_replay_dq(s, k_p, v_p, q_r, k_r, v_r, lse_r, rowdot_r, do_r, dq_r,
-                        static_cast<hipStream_t>(stream));
+  CHECK(check_ws(ws, ws_bytes, op_workspace(s, AUGTREE_OP_REPLAY_DQ)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* kpt = ws;
+  void* krt = at(ws, tr_prompt(s, s.Hkv));
+  CHECK(transpose_range(s, k_p, s.Hkv, 0, s.P, kpt, st));
+  CHECK(transpose_branches(s, k_r, s.Hkv, krt, st));
+  return step_replay_dq(s, k_p, kpt, v_p, q_r, k_r, krt, v_r, lse_r, rowdot_r, do_r, dq_r, st);
 }
 
 augtree_status augtree_prefill_kv_bwd(const augtree_dims* dims, const void* q_p, const void* k_p,
                                       const void* v_p, const float* lse_p, const float* rowdot_p,
                                       const void* do_p, const float* dk_p_acc, const float* dv_p_acc, void* dk_p,
-                                      void* dv_p, void* stream) {
+                                      void* dv_p, void* ws, size_t ws_bytes, void* stream) {
   Shape s;
   CHECK(check_dims(dims, &s));
   PTR(q_p); PTR(k_p); PTR(v_p); PTR(lse_p); PTR(rowdot_p); PTR(do_p);
@@ -500,17 +637,26 @@ augtree_status augtree_prefill_kv_bwd(const augtree_dims* dims, const void* q_p,
   if ((dk_p_acc == nullptr) != (dv_p_acc == nullptr))
     return fail(AUGTREE_ERR_INVALID_ARGUMENT, "dk_p_acc and dv_p_acc must both be set or both be NULL");
   PTR(dk_p); PTR(dv_p);
-  return step_prefill_kv_bwd(s, q_p, k_p, v_p, lse_p, rowdot_p, do_p, dk_p_acc, dv_p_acc, dk_p, dv_p,
-                             static_cast<hipStream_t>(stream));
+  CHECK(check_ws(ws, ws_bytes, op_workspace(s, AUGTREE_OP_PREFILL_KV_BWD)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* qpt = ws;
+  void* dopt = at(ws, tr_prompt(s, s.Hq));
+  CHECK(transpose_range(s, q_p, s.Hq, 0, s.P, qpt, st));
+  CHECK(transpose_range(s, do_p, s.Hq, 0, s.P, dopt, st));
+  return step_prefill_kv_bwd(s, q_p, qpt, k_p, v_p, lse_p, rowdot_p, do_p, dopt, dk_p_acc, dv_p_acc, dk_p, dv_p,
+                             st);
 }
 
 augtree_status augtree_prefill_dq(const augtree_dims* dims, const void* q_p, const void* k_p, const void* v_p,
                                   const float* lse_p, const float* rowdot_p, const void* do_p, void* dq_p,
-                                  void* stream) {
+                                  void* ws, size_t ws_bytes, void* stream) {
   Shape s;
   CHECK(check_dims(dims, &s));
   PTR(q_p); PTR(k_p); PTR(v_p); PTR(lse_p); PTR(rowdot_p); PTR(do_p); PTR(dq_p);
-  return step_prefill_dq(s, q_p, k_p, v_p, lse_p, rowdot_p, do_p, dq_p, static_cast<hipStream_t>(stream));
+  CHECK(check_ws(ws, ws_bytes, op_workspace(s, AUGTREE_OP_PREFILL_DQ)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  CHECK(transpose_range(s, k_p, s.Hkv, 0, s.P, ws, st));
+  return step_prefill_dq(s, q_p, k_p, ws, v_p, lse_p, rowdot_p, do_p, dq_p, st);
 }
 
 // ---- compositions ----
@@ -518,12 +664,13 @@ augtree_status augtree_prefill_dq(const augtree_dims* dims, const void* q_p, con
 augtree_status augtree_prefill_fwd(const augtree_dims* dims, const void* q_p, const void* k_p,
                                    const void* v_p, void* o_p, float* lse_p, void* ws,
                                    size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   Shape s;
   CHECK(check_dims(dims, &s));
   PTR(q_p); PTR(k_p); PTR(v_p); PTR(o_p); PTR(lse_p);
-  return step_prefill_fwd(s, q_p, k_p, v_p, o_p, lse_p, static_cast<hipStream_t>(stream));
+  CHECK(check_ws(ws, ws_bytes, op_workspace(s, AUGTREE_OP_PREFILL_FWD)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  CHECK(transpose_range(s, v_p, s.Hkv, 0, s.P, ws, st));
+  return step_prefill_fwd(s, q_p, k_p, ws, o_p, lse_p, st);
 }
 
 augtree_status augtree_replay_fwd(const augtree_dims* dims, const void* k_p, const void* v_p,
@@ -535,16 +682,18 @@ augtree_status augtree_replay_fwd(const augtree_dims* dims, const void* k_p, con
   const ReplayFwdWs w = replay_fwd_ws(s);
   CHECK(check_ws(ws, ws_bytes, w.total));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const float* o_parts[2] = {reinterpret_cast<float*>(at(ws, w.o_a)), reinterpret_cast<float*>(at(ws, w.o_b))};
-  const float* l_parts[2] = {reinterpret_cast<float*>(at(ws, w.lse_a)), reinterpret_cast<float*>(at(ws, w.lse_b))};
+  float* o_parts[2] = {reinterpret_cast<float*>(at(ws, w.o_a)), reinterpret_cast<float*>(at(ws, w.o_b))};
+  float* l_parts[2] = {reinterpret_cast<float*>(at(ws, w.lse_a)), reinterpret_cast<float*>(at(ws, w.lse_b))};
+  CHECK(transpose_range(s, v_p, s.Hkv, 0, s.P, at(ws, w.vpt), st));
+  CHECK(transpose_branches(s, v_r, s.Hkv, at(ws, w.vrt), st));
   // (1) every branch row against the whole, unmasked prompt K/V: partial state a
-  CHECK(step_replay_prompt_fwd(s, k_p, v_p, q_r, 0, s.P, const_cast<float*>(o_parts[0]),
-                               const_cast<float*>(l_parts[0]), st));
+  CHECK(step_replay_prompt_fwd(s, k_p, at(ws, w.vpt), q_r, 0, s.P, o_parts[0], l_parts[0], st));
   // (2) every branch row against its own branch, causally: partial state b
-  CHECK(step_replay_local_fwd(s, q_r, k_r, v_r, const_cast<float*>(o_parts[1]), const_cast<float*>(l_parts[1]),
-                              st));
+  CHECK(step_replay_local_fwd(s, q_r, k_r, at(ws, w.vrt), o_parts[1], l_parts[1], st));
   // (3) log-sum-exp merge of a and b
-  return step_merge(s, 2, o_parts, l_parts, o_r, lse_r, st);
+  const float* co[2] = {o_parts[0], o_parts[1]};
+  const float* cl[2] = {l_parts[0], l_parts[1]};
+  return step_merge(s, 2, co, cl, o_r, lse_r, st);
 }
 
 augtree_status augtree_replay_bwd(const augtree_dims* dims, const void* k_p, const void* v_p,
@@ -561,13 +710,18 @@ augtree_status augtree_replay_bwd(const augtree_dims* dims, const void* k_p, con
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* rowdot = reinterpret_cast<float*>(at(ws, w.rowdot));
   CHECK(step_row_dot(s, s.T, o_r, do_r, rowdot, st));
+  CHECK(transpose_branches(s, q_r, s.Hq, at(ws, w.qrt), st));
+  CHECK(transpose_branches(s, do_r, s.Hq, at(ws, w.dort), st));
+  CHECK(transpose_range(s, k_p, s.Hkv, 0, s.P, at(ws, w.kpt), st));
+  CHECK(transpose_branches(s, k_r, s.Hkv, at(ws, w.krt), st));
   // prompt keys x all branches' rows (no mask): the branch sum of the prompt gradient
-  CHECK(step_replay_prompt_bwd(s, k_p, v_p, q_r, lse_r, rowdot, do_r, 0, s.P, dk_p_acc, dv_p_acc,
-                               at(ws, w.prompt), st));
+  CHECK(step_replay_prompt_bwd(s, k_p, v_p, q_r, at(ws, w.qrt), lse_r, rowdot, do_r, at(ws, w.dort), 0, s.P,
+                               dk_p_acc, dv_p_acc, at(ws, w.split), st));
   // branch keys x own-branch rows (causal)
-  CHECK(step_replay_local_bwd(s, q_r, k_r, v_r, lse_r, rowdot, do_r, dk_r, dv_r, st));
+  CHECK(step_replay_local_bwd(s, q_r, at(ws, w.qrt), k_r, v_r, lse_r, rowdot, do_r, at(ws, w.dort), dk_r, dv_r,
+                              st));
   // dQ of every branch row: prompt keys, then own-branch keys
-  return step_replay_dq(s, k_p, v_p, q_r, k_r, v_r, lse_r, rowdot, do_r, dq_r, st);
+  return step_replay_dq(s, k_p, at(ws, w.kpt), v_p, q_r, k_r, at(ws, w.krt), v_r, lse_r, rowdot, do_r, dq_r, st);
 }
 
 augtree_status augtree_prefill_bwd(const augtree_dims* dims, const void* q_p, const void* k_p,
@@ -582,12 +736,17 @@ augtree_status augtree_prefill_bwd(const augtree_dims* dims, const void* q_p, co
   if ((dk_p_acc == nullptr) != (dv_p_acc == nullptr))
     return fail(AUGTREE_ERR_INVALID_ARGUMENT, "dk_p_acc and dv_p_acc must both be set or both be NULL");
   PTR(dq_p); PTR(dk_p); PTR(dv_p);
-  CHECK(check_ws(ws, ws_bytes, prefill_bwd_ws(s)));
+  const PrefillBwdWs w = prefill_bwd_ws(s);
+  CHECK(check_ws(ws, ws_bytes, w.total));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  float* rowdot = static_cast<float*>(ws);
+  float* rowdot = reinterpret_cast<float*>(at(ws, w.rowdot));
   CHECK(step_row_dot(s, s.P, o_p, do_p, rowdot, st));
-  CHECK(step_prefill_kv_bwd(s, q_p, k_p, v_p, lse_p, rowdot, do_p, dk_p_acc, dv_p_acc, dk_p, dv_p, st));
-  return step_prefill_dq(s, q_p, k_p, v_p, lse_p, rowdot, do_p, dq_p, st);
+  CHECK(transpose_range(s, q_p, s.Hq, 0, s.P, at(ws, w.qpt), st));
+  CHECK(transpose_range(s, do_p, s.Hq, 0, s.P, at(ws, w.dopt), st));
+  CHECK(transpose_range(s, k_p, s.Hkv, 0, s.P, at(ws, w.kpt), st));
+  CHECK(step_prefill_kv_bwd(s, q_p, at(ws, w.qpt), k_p, v_p, lse_p, rowdot, do_p, at(ws, w.dopt), dk_p_acc,
+                            dv_p_acc, dk_p, dv_p, st));
+  return step_prefill_dq(s, q_p, k_p, at(ws, w.kpt), v_p, lse_p, rowdot, do_p, dq_p, st);
 }
 
 }  // extern "C"

@@ -1,5 +1,6 @@
-// Building blocks shared by the gfx950 attention kernels: MFMA wrappers, the 32x32
-// accumulator layout, and global -> LDS staging in natural and transposed form.
+// Building blocks shared by the gfx950 attention kernels: matrix-core wrappers and the
+// 32x32 accumulator layout, direct global->LDS tile loads with an XOR-swizzled LDS layout,
+// the transposed operand layout, and small wave-level helpers.
 //
 // Matrix-core conventions (one wave = 64 lanes, lane l: c = l & 31, g = l >> 5):
 //   A operand (M x K): lane holds row c and E consecutive "k slots" of half g.
@@ -9,12 +10,20 @@
 // Only the pairing of A's and B's k slots matters for a contraction, so a k slot may map to
 // any k index as long as both operands use the same map. Two maps are used:
 //   natural: slot (step s, half g, element i) -> k = s*K + g*E + i (contiguous loads),
-//   C map:   slot (s, g, i) -> k = crow(s*E + i, g), i.e. the row order in which an
-//            accumulator holds its rows, so that an fp32 accumulator tile can be reused as
-//            the next MFMA's operand (softmax probabilities, dS) without any lane exchange.
-// An operand paired with a C-map operand is staged transposed in LDS, with its rows
-// permuted inside every 16-row group (bits 2 and 3 of the row index swapped, bf16 only)
-// so that the E elements one lane needs are contiguous.
+//   C map:   slot (s, g, i) -> k = crow(s*E + i, g), the row order in which an accumulator
+//            holds its rows, so that an fp32 accumulator tile (softmax probabilities, dS)
+//            is reused as the next product's operand without any lane exchange.
+// The operand paired with a C-map operand must hold, per lane, the E values of one row at
+// the k indices of the C map. Such operands come from "transposed copies" written by the
+// transpose kernel: X^T[h][d][col] with the sequence index along col, permuted inside every
+// 16-column group by tpos() (bits 2 and 3 swapped, bf16) so that the 8 values one lane needs
+// are contiguous, and every segment (the prompt, or one branch) padded with zeros to a
+// multiple of 64 columns so that tiles never straddle segments.
+//
+// Tiles are copied from global memory into LDS by the direct-to-LDS load (each lane moves 16
+// bytes; the 64 lanes of one instruction fill 1 KB of LDS in lane order). A tile row of RB
+// bytes is stored unpadded with its 16-byte chunk j at position j ^ swz(row), which keeps
+// the 16-byte fragment reads of 16 consecutive rows on distinct LDS banks.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,33 +34,44 @@ namespace augtree {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_PTR __attribute__((address_space(3)))
 
 constexpr int kWave = 64;
-constexpr int kThreads = 256;  // 4 waves per workgroup everywhere
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kInf = __builtin_inff();
 constexpr int kMaxBranches = 128;
+constexpr int kSeg = 64;  // padding granule of transposed copies (columns)
 
 // Host-built table of the branches, passed by value as a kernel argument.
 struct BranchTable {
   int32_t G;
   int32_t off[kMaxBranches + 1];          // packed row offsets of the branches
-  int32_t tile_prefix[kMaxBranches + 1];  // first tile index of each branch
+  int32_t pad[kMaxBranches + 1];          // column offsets in transposed copies (64-aligned)
+  int32_t tile_prefix[kMaxBranches + 1];  // first tile index of each branch (kernel's tile size)
 };
 
 // Branch owning tile t (tile_prefix[b] <= t < tile_prefix[b+1]).
 __device__ inline int branch_of_tile(const BranchTable& bt, int t) {
   int lo = 0, hi = bt.G - 1;
   while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
+    const int mid = (lo + hi + 1) >> 1;
     if (bt.tile_prefix[mid] <= t) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// Dispatch hands consecutive workgroup ids to the 8 XCDs in turn; renumber them so that
+// each XCD runs one contiguous range of logical ids, whose tiles share K/V in its L2.
+__device__ inline int xcd_remap(int id, int n) {
+  const int per = n >> 3, rem = n & 7;
+  const int x = id & 7, slot = id >> 3;
+  return x * per + min(x, rem) + slot;
 }
 
 template <typename T> struct Mma;
@@ -74,26 +94,71 @@ template <> struct Mma<float> {
 
 __device__ __host__ constexpr int crow(int r, int g) { return ((r >> 2) << 3) + (g << 2) + (r & 3); }
 
-// Position of row `k` inside a transposed LDS tile (see header comment).
-template <typename T> __device__ constexpr int tpos(int k);
-template <> __device__ constexpr int tpos<bf16>(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
-template <> __device__ constexpr int tpos<float>(int k) { return k; }
+// Column of sequence index i (inside a 64-aligned tile) in a transposed copy.
+template <typename T> __device__ __host__ constexpr int tpos(int i);
+template <> __device__ __host__ constexpr int tpos<bf16>(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+template <> __device__ __host__ constexpr int tpos<float>(int i) { return i; }
 
-// First position, inside a 32-row block of a transposed tile, of the elements that step s
-// of half g reads (C map).
+// First column, inside a 32-column block of a transposed tile, of the values that step s of
+// half g reads as its C-map k slots.
 template <typename T> __device__ constexpr int tread(int s, int g);
 template <> __device__ constexpr int tread<bf16>(int s, int g) { return s * 16 + g * 8; }
 template <> __device__ constexpr int tread<float>(int s, int g) { return crow(s, g); }
 
-// ---- fragment loads ----
-template <typename T> __device__ inline typename Mma<T>::frag load_frag(const T* p);
-template <> __device__ inline bf16x8 load_frag<bf16>(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
-template <> __device__ inline float load_frag<float>(const float* p) { return *p; }
+// ---- LDS tiles: RB-byte rows, 16-byte chunks XOR-swizzled by row ----
+template <int RB>
+__device__ constexpr int swz(int row) {
+  static_assert(RB == 64 || RB == 128 || RB == 256, "tile rows are 64, 128 or 256 bytes");
+  constexpr int CPR = RB / 16;  // chunks per row; 16 / CPR rows share one 256-byte bank line
+  return (row / (16 / CPR)) % CPR;
+}
+// Byte offset of byte `b` of row `row`.
+template <int RB>
+__device__ inline int tile_off(int row, int b) {
+  return row * RB + ((((b >> 4) ^ swz<RB>(row)) << 4) | (b & 15));
+}
 
-template <typename T> __device__ inline typename Mma<T>::frag zero_frag();
-template <> __device__ inline bf16x8 zero_frag<bf16>() { bf16x8 z; for (int i = 0; i < 8; ++i) z[i] = (bf16)0.f; return z; }
-template <> __device__ inline float zero_frag<float>() { return 0.f; }
+template <typename T> __device__ inline typename Mma<T>::frag lds_frag(const char* tile_base, int off);
+template <> __device__ inline bf16x8 lds_frag<bf16>(const char* p, int off) {
+  return *reinterpret_cast<const bf16x8*>(p + off);
+}
+template <> __device__ inline float lds_frag<float>(const char* p, int off) {
+  return *reinterpret_cast<const float*>(p + off);
+}
 
+// Operand fragment of row `row`, elements [e, e + E) of a natural or transposed LDS tile.
+template <typename T, int RB>
+__device__ inline typename Mma<T>::frag tile_frag(const char* tile, int row, int e) {
+  return lds_frag<T>(tile, tile_off<RB>(row, e * (int)sizeof(T)));
+}
+
+// This wave's share of the direct-to-LDS copy of a tile of ROWS rows of RB bytes. Row r of
+// the tile is read from src + min(r, nvalid - 1) * ld bytes (rows past the valid range
+// repeat the last valid one; callers mask them). NW waves share the copy. `src` is the
+// same for the whole wave and the tile spans less than 4 GB, so each lane only carries a
+// 32-bit offset.
+template <int ROWS, int RB, int NW>
+__device__ inline void dma_tile(char* lds_tile, const char* src, uint32_t ld, int nvalid, int w, int lane) {
+  constexpr int BLOCKS = ROWS * RB / 1024;
+  static_assert(BLOCKS % NW == 0 || NW % BLOCKS == 0, "tile must split evenly over the waves");
+  constexpr int RPB = 1024 / RB;  // rows per 1 KB block
+#pragma unroll
+  for (int i = 0; i < (BLOCKS + NW - 1) / NW; ++i) {
+    const int blk = w + i * NW;
+    if (BLOCKS < NW && blk >= BLOCKS) break;
+    const int row = blk * RPB + lane / (RB / 16);
+    const int pos = lane % (RB / 16);
+    const int chunk = pos ^ swz<RB>(row);
+    const uint32_t srow = (uint32_t)min(row, nvalid - 1);
+    const uint32_t off = srow * ld + (uint32_t)(chunk * 16);
+    __builtin_amdgcn_global_load_lds(src + off, (LDS_PTR void*)(lds_tile + blk * 1024), 16, 0, 0);
+  }
+}
+
+// Waits for this wave's outstanding global loads, the direct-to-LDS copies included.
+__device__ inline void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ---- accumulator helpers ----
 // Elements s*E .. s*E+E-1 of an accumulator as an operand fragment (C map).
 template <typename T> __device__ inline typename Mma<T>::frag acc_frag(const f32x16& a, int s);
 template <> __device__ inline bf16x8 acc_frag<bf16>(const f32x16& a, int s) {
@@ -104,127 +169,64 @@ template <> __device__ inline bf16x8 acc_frag<bf16>(const f32x16& a, int s) {
 }
 template <> __device__ inline float acc_frag<float>(const f32x16& a, int s) { return a[s]; }
 
-__device__ inline f32x16 zero16() { f32x16 z; for (int i = 0; i < 16; ++i) z[i] = 0.f; return z; }
+__device__ inline f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Value of the same lane index in the other half of the wave, combined: f(x, x^32).
+__device__ inline float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum of the 8 bf16 values of a fragment (as the matrix cores see them) added to acc.
+__device__ inline float frag_sum(const bf16x8& f, float acc) {
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 p = {f[2 * i], f[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(p, one, acc, false);
+  }
+  return acc;
+}
+__device__ inline float frag_sum(float f, float acc) { return acc + f; }
 
 // ---- output stores of an accumulator run of 4 consecutive elements ----
 template <typename T> __device__ inline void store4(T* p, float a, float b, float c, float d);
 template <> __device__ inline void store4<bf16>(bf16* p, float a, float b, float c, float d) {
-  bf16x4 v; v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
+  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
   *reinterpret_cast<bf16x4*>(p) = v;
 }
 template <> __device__ inline void store4<float>(float* p, float a, float b, float c, float d) {
-  f32x4 v; v[0] = a; v[1] = b; v[2] = c; v[3] = d;
+  f32x4 v = {a, b, c, d};
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
 template <typename T> __device__ inline f32x4 load4f(const T* p);
 template <> __device__ inline f32x4 load4f<bf16>(const bf16* p) {
-  bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
-  f32x4 r; r[0] = (float)v[0]; r[1] = (float)v[1]; r[2] = (float)v[2]; r[3] = (float)v[3];
-  return r;
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 template <> __device__ inline f32x4 load4f<float>(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
-__device__ inline float wave_swap_halves(float x) { return __shfl_xor(x, 32, 64); }
-
-// ---------------------------------------------------------------------------------------
-// Staging of a ROWS x D tile (rows of a [rows][H][D] tensor, row stride `ld` elements) into
-// LDS. Rows at or beyond `nvalid` are filled with zeros.
-// ---------------------------------------------------------------------------------------
-template <typename T, int D, int ROWS>
-struct Stage {
-  static constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
-  static constexpr int CH = D / EPC;               // chunks per row
-  static constexpr int NP = D + EPC;               // natural pitch (elements), 16 B pad
-  static constexpr int TP = ROWS + EPC;            // transposed pitch (elements), 16 B pad
-  static constexpr int NAT_ELEMS = ROWS * NP;
-  static constexpr int TR_ELEMS = D * TP;
-  static constexpr int NAT_UNITS = ROWS * CH;         // 16 B chunks
-  static constexpr int TR_UNITS = (ROWS / 4) * CH;    // 4-row groups
-  static constexpr int NAT_PER_THREAD = (NAT_UNITS + kThreads - 1) / kThreads;
-  static constexpr int TR_PER_THREAD = (TR_UNITS + kThreads - 1) / kThreads;
-  static_assert(NAT_UNITS % kThreads == 0 || NAT_UNITS < kThreads, "natural staging split");
-  static_assert(TR_UNITS % kThreads == 0 || TR_UNITS < kThreads, "transposed staging split");
-
-  struct NatRegs { u32x4 v[NAT_PER_THREAD]; };
-  struct TrRegs { u32x4 v[TR_PER_THREAD][4]; };
-
-  // natural: chunk c = tid + i*256 -> row c / CH, chunk c % CH (16 lanes span a row)
-  __device__ static inline void load_nat(NatRegs& r, const T* src, int64_t ld, int nvalid, int tid) {
+// Operand fragment straight from global memory (E consecutive elements).
+template <typename T> __device__ inline typename Mma<T>::frag gload_frag(const T* p);
+template <> __device__ inline bf16x8 gload_frag<bf16>(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+template <> __device__ inline float gload_frag<float>(const float* p) { return *p; }
+template <typename T> __device__ inline typename Mma<T>::frag zero_frag();
+template <> __device__ inline bf16x8 zero_frag<bf16>() {
+  bf16x8 z;
 #pragma unroll
-    for (int i = 0; i < NAT_PER_THREAD; ++i) {
-      int c = tid + i * kThreads;
-      int row = c / CH, cc = c % CH;
-      if (c < NAT_UNITS && row < nvalid) r.v[i] = *reinterpret_cast<const u32x4*>(src + row * ld + cc * EPC);
-      else r.v[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ static inline void store_nat(const NatRegs& r, T* lds, int tid) {
-#pragma unroll
-    for (int i = 0; i < NAT_PER_THREAD; ++i) {
-      int c = tid + i * kThreads;
-      int row = c / CH, cc = c % CH;
-      if (c < NAT_UNITS) *reinterpret_cast<u32x4*>(lds + row * NP + cc * EPC) = r.v[i];
-    }
-  }
-  // transposed: group q = tid + i*256 -> rows 4m..4m+3 with m = q % (ROWS/4), chunk q / (ROWS/4)
-  __device__ static inline void load_tr(TrRegs& r, const T* src, int64_t ld, int nvalid, int tid) {
-#pragma unroll
-    for (int i = 0; i < TR_PER_THREAD; ++i) {
-      int q = tid + i * kThreads;
-      int m = q % (ROWS / 4), cc = q / (ROWS / 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int row = 4 * m + j;
-        if (q < TR_UNITS && row < nvalid) r.v[i][j] = *reinterpret_cast<const u32x4*>(src + row * ld + cc * EPC);
-        else r.v[i][j] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-  // Writes the rows held as 4-row groups (load_tr) in natural layout, so that one set of
-  // global loads feeds both LDS copies of a tile.
-  __device__ static inline void store_nat_from_tr(const TrRegs& r, T* lds, int tid) {
-#pragma unroll
-    for (int i = 0; i < TR_PER_THREAD; ++i) {
-      int q = tid + i * kThreads;
-      int m = q % (ROWS / 4), cc = q / (ROWS / 4);
-      if (q >= TR_UNITS) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<u32x4*>(lds + (4 * m + j) * NP + cc * EPC) = r.v[i][j];
-    }
-  }
-  // Writes each 4-row group transposed: LDS row (chunk*EPC + e) receives elements e of
-  // rows 4m..4m+3 at position tpos(4m) (4 contiguous elements: 8 B for bf16, 16 B for f32).
-  __device__ static inline void store_tr(const TrRegs& r, T* lds, int tid) {
-#pragma unroll
-    for (int i = 0; i < TR_PER_THREAD; ++i) {
-      int q = tid + i * kThreads;
-      int m = q % (ROWS / 4), cc = q / (ROWS / 4);
-      int col = tpos<T>(4 * m);
-      if (q >= TR_UNITS) continue;
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uint32_t w[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) w[j] = (r.v[i][j][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-          u32x2 out;
-          out[0] = w[0] | (w[1] << 16);
-          out[1] = w[2] | (w[3] << 16);
-          *reinterpret_cast<u32x2*>(lds + (cc * 8 + e) * TP + col) = out;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          u32x4 out;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) out[j] = r.v[i][j][e];
-          *reinterpret_cast<u32x4*>(lds + (cc * 4 + e) * TP + col) = out;
-        }
-      }
-    }
-  }
-};
+  for (int i = 0; i < 8; ++i) z[i] = (bf16)0.f;
+  return z;
+}
+template <> __device__ inline float zero_frag<float>() { return 0.f; }
 
 }  // namespace augtree

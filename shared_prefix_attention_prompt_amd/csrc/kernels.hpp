@@ -8,22 +8,33 @@
 
 namespace augtree {
 
-// ---- forward: one Q tile of 128 rows x one query head per workgroup ----
+// ---- transposed copies: X [rows][H][D] -> X^T [H][D][cols] (see common.hpp) ----
+struct TransposeArgs {
+  const void* src;      // [rows][H][D]
+  void* dst;            // [H][D][cols]
+  int32_t H;
+  int32_t cols;         // padded columns (multiple of 64)
+  int32_t nseg;         // segments: 1 (prompt or a prompt key range) or G (branches)
+  BranchTable seg;      // off: source row offsets; pad: column offsets; tile_prefix: pad/64
+};
+
+// ---- forward: query rows x HG heads per workgroup, 64-key LDS stages ----
 enum FwdMode { kFwdPrefill = 0, kFwdReplayPrompt = 1, kFwdReplayLocal = 2 };
-constexpr int kFwdBM = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kFwdBN = 64;   // keys per LDS stage
 
 struct FwdArgs {
   const void* q;      // [nq_rows][Hq][D]
   const void* k;      // [nkv_rows][Hkv][D]
-  const void* v;
+  const void* vt;     // transposed copy of V: [Hkv][D][vt_cols]
   void* o;            // [nq_rows][Hq][D], dtype (prefill) or float32 (replay partials)
   float* lse;         // [Hq][nq_rows]
   int32_t Hq, Hkv;
   int32_t nq_rows, nkv_rows;
-  int32_t ntiles;     // query tiles per head
+  int32_t vt_cols;
+  int32_t ntiles;     // query tiles per head slot
+  int32_t nwg;        // workgroups in the grid
   float scale_log2;   // softmax scale * log2(e)
-  BranchTable bt;     // replay-local only: branch offsets and per-branch tile prefix
+  BranchTable bt;     // replay-local: branch offsets, transposed-copy offsets, tile prefix
 };
 
 // ---- merge of partial states (normalised output + LSE) per (row, head) ----
@@ -45,37 +56,43 @@ struct RowDotArgs {   // Dv[h][r] = sum_d dO[r][h][d] * O[r][h][d]
 };
 
 enum DkdvMode { kDkdvPromptFromReplay = 0, kDkdvLocal = 1, kDkdvPrefill = 2 };
-constexpr int kDkdvBN = 128;  // keys per workgroup (4 waves x 32)
-constexpr int kDkdvBM = 64;   // query rows per LDS stage
+constexpr int kDkdvBM = 32;   // query rows per LDS stage
 
 struct DkdvArgs {
   const void* q; const void* dout;         // [nq_rows][Hq][D]
+  const void* qt; const void* dot;         // transposed copies [Hq][D][qt_cols]
   const float* lse; const float* rowdot;   // [Hq][nq_rows]
   const void* k; const void* v;            // [nkv_rows][Hkv][D]
   void* dk; void* dv;                      // [nkv_rows][Hkv][D]: dtype, or float32 partials
   const float* init_dk; const float* init_dv;  // prefill: float32 [nkv][Hkv][D] added, or NULL
   int32_t Hq, Hkv;
-  int32_t nq_rows, nkv_rows;
+  int32_t nq_rows, nkv_rows, qt_cols;
   int32_t nktiles;    // key tiles per kv head
-  int32_t nsplit;     // prompt-from-replay: query range split count
+  int32_t nqtiles;    // prompt-from-replay: query tiles (32-row tiles of every branch)
+  int32_t nsplit;     // prompt-from-replay: query tile range split count
+  int32_t causal;     // 1: a key only sees queries at or after it (branch and prefill walks)
+  int32_t nwg;
   int64_t split_stride;  // elements between split partial buffers
   float scale, scale_log2;
-  BranchTable bt;     // local only (tile_prefix in units of kDkdvBN keys)
+  BranchTable bt;     // branches: offsets, padded offsets, tile prefix (query tiles for
+                      // prompt-from-replay, key tiles for the branch walk)
 };
 
 enum DqMode { kDqResponse = 0, kDqPrefill = 1 };
-constexpr int kDqBM = 128;
 constexpr int kDqBN = 64;
 
 struct DqArgs {
   const void* q; const void* dout;         // [nq_rows][Hq][D]
   const float* lse; const float* rowdot;   // [Hq][nq_rows]
   const void* k; const void* v;            // own keys: prompt (prefill) or response (response)
+  const void* kt;                          // transposed copy of own keys [Hkv][D][kt_cols]
   const void* kp; const void* vp;          // response mode: the prompt keys/values
+  const void* kpt;                         // response mode: transposed prompt keys
   void* dq;                                // [nq_rows][Hq][D]
   int32_t Hq, Hkv;
-  int32_t nq_rows, nkv_rows, nprompt;
+  int32_t nq_rows, nkv_rows, nprompt, kt_cols, kpt_cols;
   int32_t ntiles;
+  int32_t nwg;
   float scale, scale_log2;
   BranchTable bt;
 };
@@ -87,11 +104,19 @@ struct SplitReduceArgs {   // out[i] = sum_s part[s][i], s = 0..nsplit-1 in orde
   int32_t nsplit;
 };
 
+// Rows of one workgroup tile and heads per workgroup for a query-stationary kernel:
+// 4 waves of 32 rows; the waves of a workgroup cover hg query heads of one kv group.
+int heads_per_wg(int group);
+int fwd_rows_per_wg(int group);
+
+hipError_t launch_transpose(int dtype, int D, const TransposeArgs& a, hipStream_t s);
 hipError_t launch_attn_fwd(int dtype, int D, int mode, const FwdArgs& a, hipStream_t s);
 hipError_t launch_merge(int dtype, int D, const MergeArgs& a, hipStream_t s);
 hipError_t launch_rowdot(int dtype, int D, const RowDotArgs& a, hipStream_t s);
 hipError_t launch_dkdv(int dtype, int D, int mode, const DkdvArgs& a, hipStream_t s);
 hipError_t launch_dq(int dtype, int D, int mode, const DqArgs& a, hipStream_t s);
-hipError_t launch_split_reduce(const SplitReduceArgs& a, int nsplit_pairs, hipStream_t s);
+hipError_t launch_split_reduce(const SplitReduceArgs& a, hipStream_t s);
+
+constexpr int kDkdvKeysPerWG = 256;  // 8 waves x 32 keys
 
 }  // namespace augtree

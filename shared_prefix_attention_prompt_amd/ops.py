@@ -192,26 +192,42 @@ class Tree:
     def empty(self, *shape, dtype=None):
         return torch.empty(*shape, dtype=self.dtype if dtype is None else dtype, device=self.device)
 
+    def workspace_bytes(self, op: int) -> int:
+        return _lib.workspace_bytes(self.dims, op)
+
+    def workspace(self, op: int, ws=None):
+        """(pointer, bytes) of a workspace for operation `op`: `ws` when given (a uint8 GPU
+        tensor of at least the needed size), else a new one."""
+        n = self.workspace_bytes(op)
+        if ws is None:
+            ws = torch.empty(max(n, 1), dtype=torch.uint8, device=self.device)
+        elif ws.numel() < n:
+            raise ValueError(f"workspace of {ws.numel()} bytes, {n} needed")
+        self._ws_alive = ws
+        return ws.data_ptr(), ws.numel()
+
 
 def replay_prompt_fwd(tr: Tree, k_p, v_p, q_r, key_begin: int = 0, key_end: Optional[int] = None,
-                      out=None):
+                      out=None, ws=None):
     """Partial state (o_part float32 [T][Hq][D], lse_part [Hq][T]) of every branch row over
     prompt keys [key_begin, key_end)."""
     key_end = tr.P if key_end is None else key_end
     o, l = out if out is not None else (tr.empty(tr.T, tr.Hq, tr.D, dtype=torch.float32),
                                         tr.empty(tr.Hq, tr.T, dtype=torch.float32))
+    wp, wn = tr.workspace(_lib.AUGTREE_OP_REPLAY_PROMPT_FWD, ws)
     st = _lib.augtree_replay_prompt_fwd(tr.dims, k_p.data_ptr(), v_p.data_ptr(), q_r.data_ptr(), key_begin,
-                                        key_end, o.data_ptr(), l.data_ptr(), tr.stream())
+                                        key_end, o.data_ptr(), l.data_ptr(), wp, wn, tr.stream())
     _lib._check(st, "augtree_replay_prompt_fwd")
     return o, l
 
 
-def replay_local_fwd(tr: Tree, q_r, k_r, v_r, out=None):
+def replay_local_fwd(tr: Tree, q_r, k_r, v_r, out=None, ws=None):
     """Partial state of every branch row over its own branch (causal)."""
     o, l = out if out is not None else (tr.empty(tr.T, tr.Hq, tr.D, dtype=torch.float32),
                                         tr.empty(tr.Hq, tr.T, dtype=torch.float32))
+    wp, wn = tr.workspace(_lib.AUGTREE_OP_REPLAY_LOCAL_FWD, ws)
     st = _lib.augtree_replay_local_fwd(tr.dims, q_r.data_ptr(), k_r.data_ptr(), v_r.data_ptr(), o.data_ptr(),
-                                       l.data_ptr(), tr.stream())
+                                       l.data_ptr(), wp, wn, tr.stream())
     _lib._check(st, "augtree_replay_local_fwd")
     return o, l
 
@@ -242,46 +258,48 @@ def replay_prompt_bwd(tr: Tree, k_p, v_p, q_r, lse_r, rowdot_r, do_r, key_begin:
     if dk_acc is None:
         dk_acc = tr.empty(tr.P, tr.Hkv, tr.D, dtype=torch.float32)
         dv_acc = tr.empty(tr.P, tr.Hkv, tr.D, dtype=torch.float32)
-    n = _lib.workspace_bytes(tr.dims, _lib.AUGTREE_OP_REPLAY_PROMPT_BWD)
-    if ws is None and n:
-        ws = torch.empty(n, dtype=torch.uint8, device=tr.device)
+    wp, wn = tr.workspace(_lib.AUGTREE_OP_REPLAY_PROMPT_BWD, ws)
     st = _lib.augtree_replay_prompt_bwd(tr.dims, k_p.data_ptr(), v_p.data_ptr(), q_r.data_ptr(), lse_r.data_ptr(),
                                         rowdot_r.data_ptr(), do_r.data_ptr(), key_begin, key_end, dk_acc.data_ptr(),
-                                        dv_acc.data_ptr(), _ptr(ws), n, tr.stream())
+                                        dv_acc.data_ptr(), wp, wn, tr.stream())
     _lib._check(st, "augtree_replay_prompt_bwd")
     return dk_acc, dv_acc
 
 
-def replay_local_bwd(tr: Tree, q_r, k_r, v_r, lse_r, rowdot_r, do_r, out=None):
+def replay_local_bwd(tr: Tree, q_r, k_r, v_r, lse_r, rowdot_r, do_r, out=None, ws=None):
     dk, dv = out if out is not None else (torch.empty_like(k_r), torch.empty_like(v_r))
+    wp, wn = tr.workspace(_lib.AUGTREE_OP_REPLAY_LOCAL_BWD, ws)
     st = _lib.augtree_replay_local_bwd(tr.dims, q_r.data_ptr(), k_r.data_ptr(), v_r.data_ptr(), lse_r.data_ptr(),
                                        rowdot_r.data_ptr(), do_r.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                                       tr.stream())
+                                       wp, wn, tr.stream())
     _lib._check(st, "augtree_replay_local_bwd")
     return dk, dv
 
 
-def replay_dq(tr: Tree, k_p, v_p, q_r, k_r, v_r, lse_r, rowdot_r, do_r, out=None):
+def replay_dq(tr: Tree, k_p, v_p, q_r, k_r, v_r, lse_r, rowdot_r, do_r, out=None, ws=None):
     dq = out if out is not None else torch.empty_like(q_r)
+    wp, wn = tr.workspace(_lib.AUGTREE_OP_REPLAY_DQ, ws)
     st = _lib.augtree_replay_dq(tr.dims, k_p.data_ptr(), v_p.data_ptr(), q_r.data_ptr(), k_r.data_ptr(),
                                 v_r.data_ptr(), lse_r.data_ptr(), rowdot_r.data_ptr(), do_r.data_ptr(),
-                                dq.data_ptr(), tr.stream())
+                                dq.data_ptr(), wp, wn, tr.stream())
     _lib._check(st, "augtree_replay_dq")
     return dq
 
 
-def prefill_kv_bwd(tr: Tree, q_p, k_p, v_p, lse_p, rowdot_p, do_p, dk_acc=None, dv_acc=None, out=None):
+def prefill_kv_bwd(tr: Tree, q_p, k_p, v_p, lse_p, rowdot_p, do_p, dk_acc=None, dv_acc=None, out=None, ws=None):
     dk, dv = out if out is not None else (torch.empty_like(k_p), torch.empty_like(v_p))
+    wp, wn = tr.workspace(_lib.AUGTREE_OP_PREFILL_KV_BWD, ws)
     st = _lib.augtree_prefill_kv_bwd(tr.dims, q_p.data_ptr(), k_p.data_ptr(), v_p.data_ptr(), lse_p.data_ptr(),
                                      rowdot_p.data_ptr(), do_p.data_ptr(), _ptr(dk_acc), _ptr(dv_acc),
-                                     dk.data_ptr(), dv.data_ptr(), tr.stream())
+                                     dk.data_ptr(), dv.data_ptr(), wp, wn, tr.stream())
     _lib._check(st, "augtree_prefill_kv_bwd")
     return dk, dv
 
 
-def prefill_dq(tr: Tree, q_p, k_p, v_p, lse_p, rowdot_p, do_p, out=None):
+def prefill_dq(tr: Tree, q_p, k_p, v_p, lse_p, rowdot_p, do_p, out=None, ws=None):
     dq = out if out is not None else torch.empty_like(q_p)
+    wp, wn = tr.workspace(_lib.AUGTREE_OP_PREFILL_DQ, ws)
     st = _lib.augtree_prefill_dq(tr.dims, q_p.data_ptr(), k_p.data_ptr(), v_p.data_ptr(), lse_p.data_ptr(),
-                                 rowdot_p.data_ptr(), do_p.data_ptr(), dq.data_ptr(), tr.stream())
+                                 rowdot_p.data_ptr(), do_p.data_ptr(), dq.data_ptr(), wp, wn, tr.stream())
     _lib._check(st, "augtree_prefill_dq")
     return dq

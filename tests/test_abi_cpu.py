@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert _lib.abi_version() == 1
+    assert _lib.abi_version() == 2
     assert _lib.status_string(_lib.AUGTREE_OK) == "AUGTREE_OK"
     assert _lib.status_string(_lib.AUGTREE_ERR_WORKSPACE) == "AUGTREE_ERR_WORKSPACE"
     assert _lib.status_string(99) == "AUGTREE_ERR_UNKNOWN"
@@ -48,14 +48,26 @@ def _dims(P=16, off=(0, 4, 9), Hq=4, Hkv=2, D=128, scale=0.088, dtype=_lib.AUGTR
 
 
 def test_workspace_sizes():
+    # transposed copies: [H][D][cols] bf16 with the prompt padded to 64 columns and every
+    # branch padded to 64 columns on its own (30 -> 64, 40 -> 64)
     d, keep = _dims(P=100, off=(0, 30, 70), Hq=4, Hkv=2, D=128)
-    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_PREFILL_FWD) == 0
-    T, Hq, D = 70, 4, 128
+    T, P, Hq, Hkv, D = 70, 100, 4, 2, 128
+    vp_t = Hkv * D * 128 * 2
+    resp_kv_t = Hkv * D * 128 * 2
+    resp_q_t = Hq * D * 128 * 2
+    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_PREFILL_FWD) == vp_t
+    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_PROMPT_FWD) == vp_t
+    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_LOCAL_FWD) == resp_kv_t
+    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_LOCAL_BWD) == 2 * resp_q_t
+    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_DQ) == vp_t + resp_kv_t
+    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_PREFILL_KV_BWD) == 2 * Hq * D * 128 * 2
+    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_PREFILL_DQ) == vp_t
+    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_PROMPT_BWD) >= 2 * resp_q_t
     rf = _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_FWD)
-    assert rf >= 2 * T * Hq * D * 4 + 2 * T * Hq * 4
-    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_BWD) >= T * Hq * 4
-    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_PREFILL_BWD) >= 100 * Hq * 4
-    assert _lib.workspace_bytes(d, 7) == 0
+    assert rf >= 2 * T * Hq * D * 4 + 2 * T * Hq * 4 + vp_t + resp_kv_t
+    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_BWD) >= T * Hq * 4 + 2 * resp_q_t + vp_t + resp_kv_t
+    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_PREFILL_BWD) >= P * Hq * 4 + 2 * Hq * D * 128 * 2 + vp_t
+    assert _lib.workspace_bytes(d, 99) == 0
     bad, keep2 = _dims(off=(0, 4, 4))
     assert _lib.workspace_bytes(bad, _lib.AUGTREE_OP_REPLAY_FWD) == 0
 
@@ -114,6 +126,13 @@ def test_missing_or_small_workspace_rejected():
     assert st == _lib.AUGTREE_ERR_WORKSPACE and "aligned" in _lib.last_error()
     need_b = _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_BWD)
     st = _lib.augtree_replay_bwd(d, *([FAKE] * 13), None, need_b, None)
+    assert st == _lib.AUGTREE_ERR_WORKSPACE
+    need_p = _lib.workspace_bytes(d, _lib.AUGTREE_OP_PREFILL_FWD)
+    st = _lib.augtree_prefill_fwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need_p - 1, None)
+    assert st == _lib.AUGTREE_ERR_WORKSPACE
+    st = _lib.augtree_replay_local_fwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == _lib.AUGTREE_ERR_WORKSPACE
+    st = _lib.augtree_prefill_dq(d, *([FAKE] * 7), None, 0, None)
     assert st == _lib.AUGTREE_ERR_WORKSPACE
 
 
