@@ -116,6 +116,9 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 size_t tr_bytes(const Shape& s, int H, int cols) { return align_up((size_t)H * s.D * cols * s.esz()); }
 size_t tr_prompt(const Shape& s, int H) { return tr_bytes(s, H, pad64(s.P)); }
 size_t tr_resp(const Shape& s, int H) { return tr_bytes(s, H, s.Tp()); }
+// Row statistics of the key-stationary kernels: [2][Hq][cols] float32.
+size_t st_prompt(const Shape& s) { return align_up((size_t)2 * s.Hq * pad64(s.P) * sizeof(float)); }
+size_t st_resp(const Shape& s) { return align_up((size_t)2 * s.Hq * s.Tp() * sizeof(float)); }
 
 // Split count of the prompt dK/dV pass over the branches' rows for `nkeys` prompt keys:
 // enough workgroups (one per compute unit at a time) for about two rounds on 256 compute
@@ -176,13 +179,14 @@ ReplayFwdWs replay_fwd_ws(const Shape& s) {
   return w;
 }
 
-struct ReplayBwdWs { size_t rowdot, qrt, dort, kpt, krt, split, total; };
+struct ReplayBwdWs { size_t rowdot, qrt, dort, stats, kpt, krt, split, total; };
 ReplayBwdWs replay_bwd_ws(const Shape& s) {
   ReplayBwdWs w;
   Layout l;
   w.rowdot = l.add((size_t)s.T * s.Hq * sizeof(float));
   w.qrt = l.add(tr_resp(s, s.Hq));
   w.dort = l.add(tr_resp(s, s.Hq));
+  w.stats = l.add(st_resp(s));
   w.kpt = l.add(tr_prompt(s, s.Hkv));
   w.krt = l.add(tr_resp(s, s.Hkv));
   w.split = l.add(prompt_split_ws(s));
@@ -190,13 +194,14 @@ ReplayBwdWs replay_bwd_ws(const Shape& s) {
   return w;
 }
 
-struct PrefillBwdWs { size_t rowdot, qpt, dopt, kpt, total; };
+struct PrefillBwdWs { size_t rowdot, qpt, dopt, stats, kpt, total; };
 PrefillBwdWs prefill_bwd_ws(const Shape& s) {
   PrefillBwdWs w;
   Layout l;
   w.rowdot = l.add((size_t)s.P * s.Hq * sizeof(float));
   w.qpt = l.add(tr_prompt(s, s.Hq));
   w.dopt = l.add(tr_prompt(s, s.Hq));
+  w.stats = l.add(st_prompt(s));
   w.kpt = l.add(tr_prompt(s, s.Hkv));
   w.total = l.total;
   return w;
@@ -208,12 +213,12 @@ size_t op_workspace(const Shape& s, int op) {
     case AUGTREE_OP_REPLAY_FWD: return replay_fwd_ws(s).total;
     case AUGTREE_OP_REPLAY_BWD: return replay_bwd_ws(s).total;
     case AUGTREE_OP_PREFILL_BWD: return prefill_bwd_ws(s).total;
-    case AUGTREE_OP_REPLAY_PROMPT_BWD: return 2 * tr_resp(s, s.Hq) + prompt_split_ws(s);
+    case AUGTREE_OP_REPLAY_PROMPT_BWD: return 2 * tr_resp(s, s.Hq) + st_resp(s) + prompt_split_ws(s);
     case AUGTREE_OP_REPLAY_PROMPT_FWD: return tr_prompt(s, s.Hkv);
     case AUGTREE_OP_REPLAY_LOCAL_FWD: return tr_resp(s, s.Hkv);
-    case AUGTREE_OP_REPLAY_LOCAL_BWD: return 2 * tr_resp(s, s.Hq);
+    case AUGTREE_OP_REPLAY_LOCAL_BWD: return 2 * tr_resp(s, s.Hq) + st_resp(s);
     case AUGTREE_OP_REPLAY_DQ: return tr_prompt(s, s.Hkv) + tr_resp(s, s.Hkv);
-    case AUGTREE_OP_PREFILL_KV_BWD: return 2 * tr_prompt(s, s.Hq);
+    case AUGTREE_OP_PREFILL_KV_BWD: return 2 * tr_prompt(s, s.Hq) + st_prompt(s);
     case AUGTREE_OP_PREFILL_DQ: return tr_prompt(s, s.Hkv);
   }
   return 0;
@@ -284,6 +289,34 @@ augtree_status transpose_branches(const Shape& s, const void* x, int H, void* ds
     a.seg.tile_prefix[i] = s.pad[i] / kSeg;
   }
   LAUNCH(launch_transpose(s.dtype, s.D, a, st), "transposed copy (branches)");
+  return AUGTREE_OK;
+}
+
+// Row statistics (lse * log2(e), rowdot) of the prompt rows or the branch rows in the
+// column order of the matching transposed copies.
+augtree_status pack_stats_prompt(const Shape& s, const float* lse, const float* rowdot, float* out, hipStream_t st) {
+  StatPackArgs a;
+  memset(&a, 0, sizeof(a));
+  a.lse = lse; a.rowdot = rowdot; a.out = out;
+  a.H = s.Hq; a.rows = s.P; a.row0 = 0; a.cols = pad64(s.P); a.nseg = 1;
+  a.seg.G = 1; a.seg.off[1] = s.P; a.seg.pad[1] = a.cols; a.seg.tile_prefix[1] = a.cols / kSeg;
+  LAUNCH(launch_statpack(a, st), "row statistics (prompt)");
+  return AUGTREE_OK;
+}
+
+augtree_status pack_stats_branches(const Shape& s, const float* lse, const float* rowdot, float* out,
+                                   hipStream_t st) {
+  StatPackArgs a;
+  memset(&a, 0, sizeof(a));
+  a.lse = lse; a.rowdot = rowdot; a.out = out;
+  a.H = s.Hq; a.rows = s.T; a.row0 = 0; a.cols = s.Tp(); a.nseg = s.G;
+  a.seg.G = s.G;
+  for (int i = 0; i <= s.G; ++i) {
+    a.seg.off[i] = s.off[i];
+    a.seg.pad[i] = s.pad[i];
+    a.seg.tile_prefix[i] = s.pad[i] / kSeg;
+  }
+  LAUNCH(launch_statpack(a, st), "row statistics (branches)");
   return AUGTREE_OK;
 }
 
@@ -366,9 +399,8 @@ augtree_status step_row_dot(const Shape& s, int rows, const void* o, const void*
 
 // qrt/dort: transposed branch copies of q_r / do_r; split: split-partial workspace
 augtree_status step_replay_prompt_bwd(const Shape& s, const void* k_p, const void* v_p, const void* q_r,
-                                      const void* qrt, const float* lse_r, const float* rowdot_r, const void* do_r,
-                                      const void* dort, int kb, int ke, float* dk_acc, float* dv_acc, void* split,
-                                      hipStream_t st) {
+                                      const void* qrt, const float* stats, const void* do_r, const void* dort,
+                                      int kb, int ke, float* dk_acc, float* dv_acc, void* split, hipStream_t st) {
   const int nkeys = ke - kb;
   const int nsplit = prompt_split(s, nkeys);
   const size_t koff = (size_t)kb * s.Hkv * s.D;
@@ -377,7 +409,7 @@ augtree_status step_replay_prompt_bwd(const Shape& s, const void* k_p, const voi
   float* part_dv = part_dk + (nsplit > 1 ? (int64_t)nsplit * part : 0);
   DkdvArgs p;
   memset(&p, 0, sizeof(p));
-  p.q = q_r; p.dout = do_r; p.qt = qrt; p.dot = dort; p.lse = lse_r; p.rowdot = rowdot_r;
+  p.q = q_r; p.dout = do_r; p.qt = qrt; p.dot = dort; p.stats = stats;
   p.k = static_cast<const char*>(k_p) + koff * s.esz();
   p.v = static_cast<const char*>(v_p) + koff * s.esz();
   p.nsplit = nsplit;
@@ -408,11 +440,11 @@ augtree_status step_replay_prompt_bwd(const Shape& s, const void* k_p, const voi
 }
 
 augtree_status step_replay_local_bwd(const Shape& s, const void* q_r, const void* qrt, const void* k_r,
-                                     const void* v_r, const float* lse_r, const float* rowdot_r, const void* do_r,
-                                     const void* dort, void* dk_r, void* dv_r, hipStream_t st) {
+                                     const void* v_r, const float* stats, const void* do_r, const void* dort,
+                                     void* dk_r, void* dv_r, hipStream_t st) {
   DkdvArgs l;
   memset(&l, 0, sizeof(l));
-  l.q = q_r; l.dout = do_r; l.qt = qrt; l.dot = dort; l.lse = lse_r; l.rowdot = rowdot_r;
+  l.q = q_r; l.dout = do_r; l.qt = qrt; l.dot = dort; l.stats = stats;
   l.k = k_r; l.v = v_r; l.dk = dk_r; l.dv = dv_r;
   l.Hq = s.Hq; l.Hkv = s.Hkv;
   l.nq_rows = s.T; l.nkv_rows = s.T; l.qt_cols = s.Tp();
@@ -445,12 +477,12 @@ augtree_status step_replay_dq(const Shape& s, const void* k_p, const void* kpt, 
 }
 
 augtree_status step_prefill_kv_bwd(const Shape& s, const void* q_p, const void* qpt, const void* k_p,
-                                   const void* v_p, const float* lse_p, const float* rowdot_p, const void* do_p,
-                                   const void* dopt, const float* dk_acc, const float* dv_acc, void* dk_p,
-                                   void* dv_p, hipStream_t st) {
+                                   const void* v_p, const float* stats, const void* do_p, const void* dopt,
+                                   const float* dk_acc, const float* dv_acc, void* dk_p, void* dv_p,
+                                   hipStream_t st) {
   DkdvArgs p;
   memset(&p, 0, sizeof(p));
-  p.q = q_p; p.dout = do_p; p.qt = qpt; p.dot = dopt; p.lse = lse_p; p.rowdot = rowdot_p;
+  p.q = q_p; p.dout = do_p; p.qt = qpt; p.dot = dopt; p.stats = stats;
   p.k = k_p; p.v = v_p; p.dk = dk_p; p.dv = dv_p;
   p.init_dk = dk_acc; p.init_dv = dv_acc;
   p.Hq = s.Hq; p.Hkv = s.Hkv;
@@ -588,11 +620,13 @@ augtree_status augtree_replay_prompt_bwd(const augtree_dims* dims, const void* k
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* qrt = ws;
   void* dort = at(ws, tr_resp(s, s.Hq));
-  void* split = at(ws, 2 * tr_resp(s, s.Hq));
+  float* stats = reinterpret_cast<float*>(at(ws, 2 * tr_resp(s, s.Hq)));
+  void* split = at(ws, 2 * tr_resp(s, s.Hq) + st_resp(s));
   CHECK(transpose_branches(s, q_r, s.Hq, qrt, st));
   CHECK(transpose_branches(s, do_r, s.Hq, dort, st));
-  return step_replay_prompt_bwd(s, k_p, v_p, q_r, qrt, lse_r, rowdot_r, do_r, dort, key_begin, key_end, dk_p_acc,
-                                dv_p_acc, split, st);
+  CHECK(pack_stats_branches(s, lse_r, rowdot_r, stats, st));
+  return step_replay_prompt_bwd(s, k_p, v_p, q_r, qrt, stats, do_r, dort, key_begin, key_end, dk_p_acc, dv_p_acc,
+                                split, st);
 }
 
 augtree_status augtree_replay_local_bwd(const augtree_dims* dims, const void* q_r, const void* k_r,
@@ -606,9 +640,11 @@ augtree_status augtree_replay_local_bwd(const augtree_dims* dims, const void* q_
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* qrt = ws;
   void* dort = at(ws, tr_resp(s, s.Hq));
+  float* stats = reinterpret_cast<float*>(at(ws, 2 * tr_resp(s, s.Hq)));
   CHECK(transpose_branches(s, q_r, s.Hq, qrt, st));
   CHECK(transpose_branches(s, do_r, s.Hq, dort, st));
-  return step_replay_local_bwd(s, q_r, qrt, k_r, v_r, lse_r, rowdot_r, do_r, dort, dk_r, dv_r, st);
+  CHECK(pack_stats_branches(s, lse_r, rowdot_r, stats, st));
+  return step_replay_local_bwd(s, q_r, qrt, k_r, v_r, stats, do_r, dort, dk_r, dv_r, st);
 }
 
 augtree_status augtree_replay_dq(const augtree_dims* dims, const void* k_p, const void* v_p, const void* q_r,
@@ -641,10 +677,11 @@ augtree_status augtree_prefill_kv_bwd(const augtree_dims* dims, const void* q_p,
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* qpt = ws;
   void* dopt = at(ws, tr_prompt(s, s.Hq));
+  float* stats = reinterpret_cast<float*>(at(ws, 2 * tr_prompt(s, s.Hq)));
   CHECK(transpose_range(s, q_p, s.Hq, 0, s.P, qpt, st));
   CHECK(transpose_range(s, do_p, s.Hq, 0, s.P, dopt, st));
-  return step_prefill_kv_bwd(s, q_p, qpt, k_p, v_p, lse_p, rowdot_p, do_p, dopt, dk_p_acc, dv_p_acc, dk_p, dv_p,
-                             st);
+  CHECK(pack_stats_prompt(s, lse_p, rowdot_p, stats, st));
+  return step_prefill_kv_bwd(s, q_p, qpt, k_p, v_p, stats, do_p, dopt, dk_p_acc, dv_p_acc, dk_p, dv_p, st);
 }
 
 augtree_status augtree_prefill_dq(const augtree_dims* dims, const void* q_p, const void* k_p, const void* v_p,
@@ -714,12 +751,13 @@ augtree_status augtree_replay_bwd(const augtree_dims* dims, const void* k_p, con
   CHECK(transpose_branches(s, do_r, s.Hq, at(ws, w.dort), st));
   CHECK(transpose_range(s, k_p, s.Hkv, 0, s.P, at(ws, w.kpt), st));
   CHECK(transpose_branches(s, k_r, s.Hkv, at(ws, w.krt), st));
+  float* stats = reinterpret_cast<float*>(at(ws, w.stats));
+  CHECK(pack_stats_branches(s, lse_r, rowdot, stats, st));
   // prompt keys x all branches' rows (no mask): the branch sum of the prompt gradient
-  CHECK(step_replay_prompt_bwd(s, k_p, v_p, q_r, at(ws, w.qrt), lse_r, rowdot, do_r, at(ws, w.dort), 0, s.P,
-                               dk_p_acc, dv_p_acc, at(ws, w.split), st));
+  CHECK(step_replay_prompt_bwd(s, k_p, v_p, q_r, at(ws, w.qrt), stats, do_r, at(ws, w.dort), 0, s.P, dk_p_acc,
+                               dv_p_acc, at(ws, w.split), st));
   // branch keys x own-branch rows (causal)
-  CHECK(step_replay_local_bwd(s, q_r, at(ws, w.qrt), k_r, v_r, lse_r, rowdot, do_r, at(ws, w.dort), dk_r, dv_r,
-                              st));
+  CHECK(step_replay_local_bwd(s, q_r, at(ws, w.qrt), k_r, v_r, stats, do_r, at(ws, w.dort), dk_r, dv_r, st));
   // dQ of every branch row: prompt keys, then own-branch keys
   return step_replay_dq(s, k_p, at(ws, w.kpt), v_p, q_r, k_r, at(ws, w.krt), v_r, lse_r, rowdot, do_r, dq_r, st);
 }
@@ -744,8 +782,10 @@ augtree_status augtree_prefill_bwd(const augtree_dims* dims, const void* q_p, co
   CHECK(transpose_range(s, q_p, s.Hq, 0, s.P, at(ws, w.qpt), st));
   CHECK(transpose_range(s, do_p, s.Hq, 0, s.P, at(ws, w.dopt), st));
   CHECK(transpose_range(s, k_p, s.Hkv, 0, s.P, at(ws, w.kpt), st));
-  CHECK(step_prefill_kv_bwd(s, q_p, at(ws, w.qpt), k_p, v_p, lse_p, rowdot, do_p, at(ws, w.dopt), dk_p_acc,
-                            dv_p_acc, dk_p, dv_p, st));
+  float* stats = reinterpret_cast<float*>(at(ws, w.stats));
+  CHECK(pack_stats_prompt(s, lse_p, rowdot, stats, st));
+  CHECK(step_prefill_kv_bwd(s, q_p, at(ws, w.qpt), k_p, v_p, stats, do_p, at(ws, w.dopt), dk_p_acc, dv_p_acc, dk_p,
+                            dv_p, st));
   return step_prefill_dq(s, q_p, k_p, at(ws, w.kpt), v_p, lse_p, rowdot, do_p, dq_p, st);
 }
 

@@ -5,7 +5,7 @@
 // where rowdot[r] = sum_d dO[r, d] O[r, d] (equal to sum_j P[r, j] dP[r, j]).
 //
 // dK/dV are computed key-stationary: a workgroup of 8 waves owns 256 keys of one key/value
-// head (32 per wave, kept in registers with their dK/dV accumulators) and walks every query
+// head (32 per wave; K and the dK/dV accumulators in registers, V in LDS) and walks every query
 // tile that can see them, for every query head mapped to that kv head, in a fixed order. For
 // the prompt keys this walk runs over all branches' rows at once, so the prompt gradient of
 // every branch is summed inside one accumulator ("Splitting Prompt Prefill from Response
@@ -17,9 +17,9 @@
 // dQ is computed query-stationary in its own pass (it recomputes S and dP), which keeps it
 // free of atomics as well.
 //
-// Query tiles (dK/dV) and key tiles (dQ) of 64 positions are copied global -> LDS by direct
-// loads, double buffered, both in natural layout and from the transposed copies (the
-// operands of the products that contract over the sequence).
+// Query tiles (dK/dV) and key tiles (dQ) are copied global -> LDS by direct loads through a
+// ring of LDS stages, both in natural layout and from the transposed copies (the operands of
+// the products that contract over the sequence).
 #include "kernels.hpp"
 
 namespace augtree {
@@ -28,27 +28,33 @@ template <typename T, typename OT, int D, int MODE>
 __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
   using M = Mma<T>;
   constexpr int NW = 8;
+  constexpr int NSTAGE = 2;  // with the workgroup's V rows resident, two stages fit in LDS
   constexpr int ESZ = sizeof(T);
   constexpr int BM = kDkdvBM;
   constexpr int RBN = D * ESZ;   // natural tile row bytes
   constexpr int RBT = BM * ESZ;  // transposed tile row bytes
-  constexpr int NT = BM * RBN, TT = D * RBT;
+  using TN = TileSrc<BM, RBN>;      // Q or dO tile, natural
+  using TT = TileSrc<D, RBT>;       // Q^T or dO^T tile, transposed
+  using TS = TileSrc<2, BM * 4>;    // row statistics: lse * log2(e), rowdot
+  using TVR = TileSrc<32 * NW, RBN>;  // the workgroup's V rows
+  constexpr int O_DO = TN::NB * 1024, O_QT = 2 * TN::NB * 1024, O_DOT = O_QT + TT::NB * 1024;
+  constexpr int O_ST = O_DOT + TT::NB * 1024;
+  constexpr int SB = O_ST + TS::NB * 1024;  // bytes per stage
+  constexpr int RD = pitch<BM * 4>() / 4;   // float offset of the rowdot row
   constexpr int KS = D / M::K, DB = D / 32, NS = 32 / M::K;
   constexpr int KPW = 32 * NW;
 
-  __shared__ __attribute__((aligned(1024))) char lv[KPW * RBN];  // this workgroup's V rows
-  __shared__ __attribute__((aligned(1024))) char lq0[NT];
-  __shared__ __attribute__((aligned(1024))) char lq1[NT];
-  __shared__ __attribute__((aligned(1024))) char lo0[NT];
-  __shared__ __attribute__((aligned(1024))) char lo1[NT];
-  __shared__ __attribute__((aligned(1024))) char lqt0[TT];
-  __shared__ __attribute__((aligned(1024))) char lqt1[TT];
-  __shared__ __attribute__((aligned(1024))) char lot0[TT];
-  __shared__ __attribute__((aligned(1024))) char lot1[TT];
-  __shared__ __attribute__((aligned(16))) float ls0[2 * BM];  // lse * log2(e), then rowdot
-  __shared__ __attribute__((aligned(16))) float ls1[2 * BM];
+  __shared__ __attribute__((aligned(1024))) char lv[TVR::NB * 1024];  // this workgroup's V rows
+  // one LDS object per stage: Q, dO (natural), Q^T, dO^T (transposed), row statistics
+  __shared__ __attribute__((aligned(1024))) char ls0[SB];
+  __shared__ __attribute__((aligned(1024))) char ls1[SB];
+  auto stage = [&](auto S) -> char* {
+    constexpr int st = decltype(S)::value;
+    if constexpr (st == 0) return ls0; else return ls1;
+  };
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lid = xcd_remap(blockIdx.x, a.nwg);
   const int per_kvh = a.nktiles * a.nsplit;
   const int kvh = lid / per_kvh;
@@ -85,14 +91,15 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
 
   const uint32_t qld = (uint32_t)(a.Hq * D * ESZ);   // bytes between query rows
   const uint32_t tld = (uint32_t)(a.qt_cols * ESZ);  // bytes between transposed rows
-  const uint32_t kld = (uint32_t)(a.Hkv * D * ESZ);  // bytes between key rows
   const int key = k0 + w * 32 + c;
   const bool kvalid = key < k1;
   const int wk_lo = k0 + w * 32;
 
-  // V rows of the workgroup's keys go to LDS once; K stays in registers.
-  dma_tile<KPW, RBN, NW>(lv, reinterpret_cast<const char*>(a.v) + ((int64_t)k0 * a.Hkv + kvh) * D * ESZ, kld,
-                         k1 - k0, w, lane);
+  // V rows of the workgroup's keys go to LDS once (landed before the pipeline's first
+  // barrier); K stays in registers.
+  dma_stage<NW>(lv, w, lane,
+                TVR{reinterpret_cast<const char*>(a.v) + ((int64_t)k0 * a.Hkv + kvh) * D * ESZ,
+                    (uint32_t)(a.Hkv * D * ESZ), k1 - k0});
   typename M::frag kf[KS];
   {
     const T* kp = reinterpret_cast<const T*>(a.k) + ((int64_t)key * a.Hkv + kvh) * D + g * M::E;
@@ -107,83 +114,78 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
   const int ntile = t_hi > t_lo ? t_hi - t_lo : 0;
   const int niter = ntile * group;
 
-  // Query tiles in walk order: for each query head of the group, tiles t_lo .. t_hi - 1.
-  // The tile being issued is tracked incrementally (branch of the tile included); compute
-  // reads what issue recorded for its stage.
+  // Query tile of iteration it: head it / ntile, tile t_lo + it % ntile.
   struct Tile { int hq, row0, col0, nval; };
-  int it_head = 0, it_t = t_lo, it_b = b;
-  if constexpr (MODE == kDkdvPromptFromReplay) it_b = t_lo < t_hi ? branch_of_tile(a.bt, t_lo) : 0;
-  const int b_first = it_b;
-  auto next_tile = [&]() {
+  auto tile_of = [&](int it) {
     Tile tl;
-    tl.hq = kvh * group + it_head;
+    tl.hq = kvh * group + it / ntile;
+    const int t = t_lo + it % ntile;
     if constexpr (MODE == kDkdvPromptFromReplay) {
-      while (it_t >= a.bt.tile_prefix[it_b + 1]) ++it_b;
-      const int j = it_t - a.bt.tile_prefix[it_b];
-      tl.row0 = a.bt.off[it_b] + j * BM;
-      tl.col0 = a.bt.pad[it_b] + j * BM;
-      tl.nval = min(BM, a.bt.off[it_b + 1] - tl.row0);
+      const int bb = branch_of_tile(a.bt, t);
+      const int j = t - a.bt.tile_prefix[bb];
+      tl.row0 = a.bt.off[bb] + j * BM;
+      tl.col0 = a.bt.pad[bb] + j * BM;
+      tl.nval = min(BM, a.bt.off[bb + 1] - tl.row0);
     } else if constexpr (MODE == kDkdvLocal) {
-      tl.row0 = a.bt.off[b] + it_t * BM;
-      tl.col0 = a.bt.pad[b] + it_t * BM;
+      tl.row0 = a.bt.off[b] + t * BM;
+      tl.col0 = a.bt.pad[b] + t * BM;
       tl.nval = min(BM, a.bt.off[b + 1] - tl.row0);
     } else {
-      tl.row0 = it_t * BM;
-      tl.col0 = it_t * BM;
+      tl.row0 = t * BM;
+      tl.col0 = t * BM;
       tl.nval = min(BM, a.nq_rows - tl.row0);
     }
-    if (++it_t == t_hi) { it_t = t_lo; it_b = b_first; ++it_head; }
     return tl;
   };
 
-  // Row statistics of the next tile: wave 0 lanes 0..31 hold lse * log2(e), lanes 32..63
-  // rowdot, one row per lane. Rows past the tile's valid range get lse = +inf, so their
-  // probabilities are 0.
-  float stat = 0.f;
-  auto issue = [&](const Tile& tl, char* q_, char* o_, char* qt_, char* ot_) {
-    const char* nat_q = reinterpret_cast<const char*>(a.q) + ((int64_t)tl.row0 * a.Hq + tl.hq) * D * ESZ;
-    const char* nat_o = reinterpret_cast<const char*>(a.dout) + ((int64_t)tl.row0 * a.Hq + tl.hq) * D * ESZ;
+  auto issue = [&](int it, auto S) {
+    const Tile tl = tile_of(it);
+    const int64_t nat = ((int64_t)tl.row0 * a.Hq + tl.hq) * D * ESZ;
     const int64_t tr = ((int64_t)tl.hq * D * a.qt_cols + tl.col0) * ESZ;
-    dma_tile<BM, RBN, NW>(q_, nat_q, qld, tl.nval, w, lane);
-    dma_tile<BM, RBN, NW>(o_, nat_o, qld, tl.nval, w, lane);
-    dma_tile<D, RBT, NW>(qt_, reinterpret_cast<const char*>(a.qt) + tr, tld, D, w, lane);
-    dma_tile<D, RBT, NW>(ot_, reinterpret_cast<const char*>(a.dot) + tr, tld, D, w, lane);
-    if (w == 0) {
-      const bool ok = c < tl.nval;
-      const int64_t si = (int64_t)tl.hq * a.nq_rows + tl.row0 + min(c, tl.nval - 1);
-      stat = g == 0 ? (ok ? a.lse[si] * kLog2e : kInf) : (ok ? a.rowdot[si] : 0.f);
-    }
-  };
-  auto publish_stat = [&](float* st) {
-    if (w == 0) st[lane] = stat;
+    dma_stage<NW>(stage(S), w, lane, TN{reinterpret_cast<const char*>(a.q) + nat, qld, tl.nval},
+                  TN{reinterpret_cast<const char*>(a.dout) + nat, qld, tl.nval},
+                  TT{reinterpret_cast<const char*>(a.qt) + tr, tld, D},
+                  TT{reinterpret_cast<const char*>(a.dot) + tr, tld, D},
+                  TS{reinterpret_cast<const char*>(a.stats + (int64_t)tl.hq * a.qt_cols + tl.col0),
+                     (uint32_t)((int64_t)a.Hq * a.qt_cols * 4), 2});
   };
 
-  auto compute = [&](const Tile& tl, const char* q_, const char* o_, const char* qt_, const char* ot_,
-                     const float* st) {
+  auto compute = [&](int it, auto S) {
+    const Tile tl = tile_of(it);
+    const char* q_ = stage(S);
+    const char* o_ = q_ + O_DO;
+    const char* qt_ = q_ + O_QT;
+    const char* ot_ = q_ + O_DOT;
+    const float* st = reinterpret_cast<const float*>(q_ + O_ST);
     const int row0 = tl.row0;
     if (causal && row0 + 31 < wk_lo) return;  // every query of the tile precedes every key
-    const bool need_mask = causal && row0 < wk_lo + 31;  // the diagonal tile
     f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       sacc = M::run(tile_frag<T, RBN>(q_, c, s * M::K + g * M::E), kf[s], sacc);
-      pacc = M::run(tile_frag<T, RBN>(o_, c, s * M::K + g * M::E), tile_frag<T, RBN>(lv, w * 32 + c, s * M::K + g * M::E),
-                    pacc);
+      pacc = M::run(tile_frag<T, RBN>(o_, c, s * M::K + g * M::E),
+                    tile_frag<T, RBN>(lv, w * 32 + c, s * M::K + g * M::E), pacc);
     }
+    auto softmax_grad = [&](auto masked) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int qi = r4 * 8 + g * 4;
-      const f32x4 L = *reinterpret_cast<const f32x4*>(st + qi);
-      const f32x4 R = *reinterpret_cast<const f32x4*>(st + BM + qi);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int qi = r4 * 8 + g * 4;
+        const f32x4 L = *reinterpret_cast<const f32x4*>(st + qi);
+        const f32x4 R = *reinterpret_cast<const f32x4*>(st + RD + qi);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = r4 * 4 + j;
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], sl2, -L[j]));
-        if (need_mask && key > row0 + qi + j) p = 0.f;
-        pacc[r] = p * (pacc[r] - R[j]);
-        sacc[r] = p;
+        for (int j = 0; j < 4; ++j) {
+          const int r = r4 * 4 + j;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], sl2, -L[j]));
+          if constexpr (decltype(masked)::value) {
+            if (key > row0 + qi + j) p = 0.f;
+          }
+          pacc[r] = p * (pacc[r] - R[j]);
+          sacc[r] = p;
+        }
       }
-    }
+    };
+    if (causal && row0 < wk_lo + 31) softmax_grad(std::true_type{});  // the diagonal tile
+    else softmax_grad(std::false_type{});
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const typename M::frag pf = acc_frag<T>(sacc, s);
@@ -196,33 +198,10 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
     }
   };
 
-  Tile t0 = {0, 0, 0, 1}, t1 = {0, 0, 0, 1};
-  if (niter > 0) {
-    t0 = next_tile();
-    issue(t0, lq0, lo0, lqt0, lot0);
-    publish_stat(ls0);
-  }
-  wait_vm();
-  __syncthreads();
-  for (int it = 0; it < niter; it += 2) {
-    if (it + 1 < niter) {
-      t1 = next_tile();
-      issue(t1, lq1, lo1, lqt1, lot1);
-    }
-    compute(t0, lq0, lo0, lqt0, lot0, ls0);
-    if (it + 1 < niter) publish_stat(ls1);
-    wait_vm();
-    __syncthreads();
-    if (it + 1 >= niter) break;
-    if (it + 2 < niter) {
-      t0 = next_tile();
-      issue(t0, lq0, lo0, lqt0, lot0);
-    }
-    compute(t1, lq1, lo1, lqt1, lot1, ls1);
-    if (it + 2 < niter) publish_stat(ls0);
-    wait_vm();
-    __syncthreads();
-  }
+  if (niter > 0)
+    run_pipeline<NSTAGE, stage_copies<NW, TN, TN, TT, TT, TS>()>(niter, issue, compute);
+  else
+    wait_vm();  // the V copy must land before the workgroup's LDS is released
 
   if (!kvalid) return;
   int64_t obase = ((int64_t)key * a.Hkv + kvh) * D;
@@ -260,18 +239,25 @@ __global__ __launch_bounds__(512, 2) void dq_kernel(DqArgs a) {
   constexpr int ESZ = sizeof(T);
   constexpr int BN = kDqBN;
   constexpr int RBN = D * ESZ, RBT = BN * ESZ;
-  constexpr int NT = BN * RBN, TT = D * RBT;
+  using TN = TileSrc<BN, RBN>;  // K or V tile, natural
+  using TT = TileSrc<D, RBT>;   // K^T tile, transposed
+  constexpr int O_V = TN::NB * 1024, O_KT = 2 * TN::NB * 1024;
+  constexpr int SB = O_KT + TT::NB * 1024;  // bytes per stage
   constexpr int KS = D / M::K, DB = D / 32, NS = 32 / M::K, KB = BN / 32;
   constexpr int RT = 32 * (NW / HG);
 
-  __shared__ __attribute__((aligned(1024))) char lk0[NT];
-  __shared__ __attribute__((aligned(1024))) char lk1[NT];
-  __shared__ __attribute__((aligned(1024))) char lv0[NT];
-  __shared__ __attribute__((aligned(1024))) char lv1[NT];
-  __shared__ __attribute__((aligned(1024))) char lkt0[TT];
-  __shared__ __attribute__((aligned(1024))) char lkt1[TT];
+  constexpr int NSTAGE = 3;
+  // one LDS object per stage: K tile, V tile, K^T tile
+  __shared__ __attribute__((aligned(1024))) char ls0[SB];
+  __shared__ __attribute__((aligned(1024))) char ls1[SB];
+  __shared__ __attribute__((aligned(1024))) char ls2[SB];
+  auto stage = [&](auto S) -> char* {
+    constexpr int st = decltype(S)::value;
+    if constexpr (st == 0) return ls0; else if constexpr (st == 1) return ls1; else return ls2;
+  };
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lid = xcd_remap(blockIdx.x, a.nwg);
   const int hs = lid / a.ntiles;
   int tile = lid % a.ntiles;
@@ -348,18 +334,19 @@ __global__ __launch_bounds__(512, 2) void dq_kernel(DqArgs a) {
     }
   };
 
-  auto issue = [&](int it, char* k_, char* v_, char* kt_) {
+  auto issue = [&](int it, auto S) {
     const char *kp, *vp, *ktp;
     uint32_t ktld;
     int ks, nv;
     bool cz;
     tile_src(it, kp, vp, ktp, ktld, ks, nv, cz);
-    dma_tile<BN, RBN, NW>(k_, kp, kld, nv, w, lane);
-    dma_tile<BN, RBN, NW>(v_, vp, kld, nv, w, lane);
-    dma_tile<D, RBT, NW>(kt_, ktp, ktld, D, w, lane);
+    dma_stage<NW>(stage(S), w, lane, TN{kp, kld, nv}, TN{vp, kld, nv}, TT{ktp, ktld, D});
   };
 
-  auto compute = [&](int it, const char* k_, const char* v_, const char* kt_) {
+  auto compute = [&](int it, auto S) {
+    const char* k_ = stage(S);
+    const char* v_ = k_ + O_V;
+    const char* kt_ = k_ + O_KT;
     const char *kp, *vp, *ktp;
     uint32_t ktld;
     int kt, nv;
@@ -395,20 +382,7 @@ __global__ __launch_bounds__(512, 2) void dq_kernel(DqArgs a) {
     }
   };
 
-  issue(0, lk0, lv0, lkt0);
-  wait_vm();
-  __syncthreads();
-  for (int it = 0; it < nkt; it += 2) {
-    if (it + 1 < nkt) issue(it + 1, lk1, lv1, lkt1);
-    compute(it, lk0, lv0, lkt0);
-    wait_vm();
-    __syncthreads();
-    if (it + 1 >= nkt) break;
-    if (it + 2 < nkt) issue(it + 2, lk0, lv0, lkt0);
-    compute(it + 1, lk1, lv1, lkt1);
-    wait_vm();
-    __syncthreads();
-  }
+  run_pipeline<NSTAGE, stage_copies<NW, TN, TN, TT>()>(nkt, issue, compute);
 
   if (!qvalid) return;
   T* out = reinterpret_cast<T*>(a.dq) + (int64_t)qrow * qld + (int64_t)h * D;

@@ -6,10 +6,10 @@
 // updates a running row maximum m, normaliser l and unnormalised output (the partial state
 // S = (m, l, O_acc) of §3.3, Fig. 8).
 //
-// A workgroup is 4 waves of 32 query rows; its waves cover HG query heads of one key/value
-// group (HG = 4 for grouped-query heads, so one staged K/V tile serves four heads), and two
-// workgroups share a compute unit. K/V tiles of 64 keys go global -> LDS by direct loads,
-// double buffered: the next tile's copy is in flight during the current tile's math.
+// A workgroup is 8 waves of 32 query rows (two per SIMD); its waves cover HG query heads of
+// one key/value group (HG = 4 for grouped-query heads, so one staged K/V tile serves four
+// heads). K/V tiles of 64 keys go global -> LDS by direct loads through a 4-stage ring: three
+// tiles are in flight while the current one is used.
 //
 // Per wave and tile: S^T = K Q^T on the matrix cores, so the accumulator holds one query per
 // lane and the softmax statistics are per lane; P^T = exp2(S^T * scale*log2e - m) is fed
@@ -25,23 +25,34 @@ namespace augtree {
 constexpr float kRescaleGap = 8.f;  // log2 of the largest unnormalised probability kept
 
 template <typename T, typename OT, int D, int MODE, int HG>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kFwdWaves * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   using M = Mma<T>;
-  constexpr int NW = 4;
+  constexpr int NW = kFwdWaves;
+  constexpr int NSTAGE = 4;  // LDS stages
   constexpr int ESZ = sizeof(T);
   constexpr int BN = kFwdBN;
   constexpr int RBK = D * ESZ;   // bytes of a natural K tile row
   constexpr int RBV = BN * ESZ;  // bytes of a transposed V tile row
-  constexpr int KT = BN * RBK, VT = D * RBV;
+  using TK = TileSrc<BN, RBK>;  // K tile, natural
+  using TV = TileSrc<D, RBV>;   // V^T tile, from the transposed copy
+  constexpr int VOFF = TK::NB * 1024;
+  constexpr int SB = (TK::NB + TV::NB) * 1024;  // bytes per stage
   constexpr int KS = D / M::K, DB = D / 32, NS = 32 / M::K, KB = BN / 32;
   constexpr int RT = 32 * (NW / HG);  // query rows per workgroup
 
-  __shared__ __attribute__((aligned(1024))) char lk0[KT];
-  __shared__ __attribute__((aligned(1024))) char lk1[KT];
-  __shared__ __attribute__((aligned(1024))) char lv0[VT];
-  __shared__ __attribute__((aligned(1024))) char lv1[VT];
+  // one LDS object per stage (K tile, then V^T tile): distinct objects keep the stages apart
+  // for the compiler
+  __shared__ __attribute__((aligned(1024))) char ls0[SB];
+  __shared__ __attribute__((aligned(1024))) char ls1[SB];
+  __shared__ __attribute__((aligned(1024))) char ls2[SB];
+  __shared__ __attribute__((aligned(1024))) char ls3[SB];
+  auto stage = [&](auto S) -> char* {
+    constexpr int st = decltype(S)::value;
+    if constexpr (st == 0) return ls0; else if constexpr (st == 1) return ls1; else if constexpr (st == 2) return ls2; else return ls3;
+  };
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lid = xcd_remap(blockIdx.x, a.nwg);
   const int hs = lid / a.ntiles;
   int tile = lid % a.ntiles;
@@ -77,10 +88,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     causal = true;
   }
 
-  const int64_t kld = (int64_t)a.Hkv * D * ESZ;  // bytes between key rows
-  const int64_t vld = (int64_t)a.vt_cols * ESZ;  // bytes between V^T rows
+  const uint32_t kld = (uint32_t)(a.Hkv * D * ESZ);  // bytes between key rows
+  const uint32_t vld = (uint32_t)(a.vt_cols * ESZ);  // bytes between V^T rows
   const char* kbase = reinterpret_cast<const char*>(a.k) + (int64_t)kvh * D * ESZ;
-  const char* vbase = reinterpret_cast<const char*>(a.vt) + (int64_t)kvh * D * vld;
+  const char* vbase = reinterpret_cast<const char*>(a.vt) + (int64_t)kvh * D * a.vt_cols * ESZ;
 
   const int wq0 = q0 + rb * 32;
   const int qrow = wq0 + c;
@@ -102,13 +113,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const float sl2 = a.scale_log2;
   const int nkt = (k1 - k0 + BN - 1) / BN;
 
-  auto issue = [&](int it, char* kbuf, char* vbuf) {
+  auto issue = [&](int it, auto S) {
     const int kt = k0 + it * BN;
-    dma_tile<BN, RBK, NW>(kbuf, kbase + kt * kld, kld, k1 - kt, w, lane);
-    dma_tile<D, RBV, NW>(vbuf, vbase + (int64_t)(vcol0 + it * BN) * ESZ, vld, D, w, lane);
+    dma_stage<NW>(stage(S), w, lane, TK{kbase + (int64_t)kt * kld, kld, k1 - kt},
+                  TV{vbase + (int64_t)(vcol0 + it * BN) * ESZ, vld, D});
   };
 
-  auto compute = [&](int it, const char* lk, const char* lv) {
+  auto compute = [&](int it, auto S) {
+    const char* lk = stage(S);
+    const char* lv = lk + VOFF;
     const int kt = k0 + it * BN;
     if (!wave_has_rows || (causal && kt > wq_hi)) return;
     f32x16 sacc[KB];
@@ -161,20 +174,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
       }
   };
 
-  issue(0, lk0, lv0);
-  wait_vm();
-  __syncthreads();
-  for (int it = 0; it < nkt; it += 2) {
-    if (it + 1 < nkt) issue(it + 1, lk1, lv1);
-    compute(it, lk0, lv0);
-    wait_vm();
-    __syncthreads();
-    if (it + 1 >= nkt) break;
-    if (it + 2 < nkt) issue(it + 2, lk0, lv0);
-    compute(it + 1, lk1, lv1);
-    wait_vm();
-    __syncthreads();
-  }
+  run_pipeline<NSTAGE, stage_copies<NW, TK, TV>()>(nkt, issue, compute);
 
   const float l = halves_sum(l_run);
   if (qvalid) {
@@ -192,11 +192,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 }
 
 int heads_per_wg(int group) { return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1); }
-int fwd_rows_per_wg(int group) { return 32 * (4 / heads_per_wg(group)); }
+int fwd_rows_per_wg(int group) { return 32 * (kFwdWaves / heads_per_wg(group)); }
 
 template <typename T, int D, int HG>
 static hipError_t launch_fwd_hg(int mode, const FwdArgs& a, hipStream_t s) {
-  dim3 grid(a.nwg), block(256);
+  dim3 grid(a.nwg), block(kFwdWaves * 64);
   switch (mode) {
     case kFwdPrefill: hipLaunchKernelGGL((attn_fwd_kernel<T, T, D, kFwdPrefill, HG>), grid, block, 0, s, a); break;
     case kFwdReplayPrompt: hipLaunchKernelGGL((attn_fwd_kernel<T, float, D, kFwdReplayPrompt, HG>), grid, block, 0, s, a); break;

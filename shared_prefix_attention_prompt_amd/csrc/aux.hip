@@ -44,6 +44,23 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
   }
 }
 
+// Row statistics of the backward in the column layout of the transposed copies, for the
+// key-stationary kernels: out[h][col] = lse * log2(e) and out[H + h][col] = rowdot of the
+// row held in that column (segment rows in natural order, every segment padded to 64
+// columns); padding columns get lse = +inf and rowdot = 0, so they carry zero probability.
+__global__ __launch_bounds__(256) void statpack_kernel(StatPackArgs a) {
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  const int h = blockIdx.y;
+  if (col >= a.cols) return;
+  const int tile = col / kSeg;
+  const int b = a.nseg == 1 ? 0 : branch_of_tile(a.seg, tile);
+  const int row = a.seg.off[b] + (col - a.seg.pad[b]);
+  const bool ok = row < a.seg.off[b + 1];
+  const int64_t src = (int64_t)h * a.rows + a.row0 + row;
+  a.out[(int64_t)h * a.cols + col] = ok ? a.lse[src] * kLog2e : kInf;
+  a.out[(int64_t)(a.H + h) * a.cols + col] = ok ? a.rowdot[src] : 0.f;
+}
+
 // Merge of the replay partial states of each (row, head), e.g. the prompt part and the
 // response-local part, or the parts of several prompt K/V shards. Each part is a normalised
 // output with its LSE; the combined LSE is m + log(sum_i e^(lse_i - m)) with m = max_i lse_i,
@@ -138,6 +155,12 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(SplitReduceArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+hipError_t launch_statpack(const StatPackArgs& a, hipStream_t s) {
+  if (a.cols == 0) return hipSuccess;
+  hipLaunchKernelGGL(statpack_kernel, dim3((a.cols + 255) / 256, a.H), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_transpose(int dtype, int D, const TransposeArgs& a, hipStream_t s) {
   if (a.cols == 0) return hipSuccess;
   dim3 grid(a.cols / 64, a.H), block(256);

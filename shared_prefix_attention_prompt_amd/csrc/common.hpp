@@ -22,12 +22,15 @@
 //
 // Tiles are copied from global memory into LDS by the direct-to-LDS load (each lane moves 16
 // bytes; the 64 lanes of one instruction fill 1 KB of LDS in lane order). A tile row of RB
-// bytes is stored unpadded with its 16-byte chunk j at position j ^ swz(row), which keeps
-// the 16-byte fragment reads of 16 consecutive rows on distinct LDS banks.
+// bytes is stored at a pitch of RB + 16 bytes, which keeps the 16-byte fragment reads of 16
+// consecutive rows on distinct LDS banks and every read address an immediate offset from one
+// per-lane base; the lane whose 16 bytes land on a row's pad slot copies any valid chunk.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace augtree {
 
@@ -105,18 +108,18 @@ template <typename T> __device__ constexpr int tread(int s, int g);
 template <> __device__ constexpr int tread<bf16>(int s, int g) { return s * 16 + g * 8; }
 template <> __device__ constexpr int tread<float>(int s, int g) { return crow(s, g); }
 
-// ---- LDS tiles: RB-byte rows, 16-byte chunks XOR-swizzled by row ----
+// ---- LDS tiles: RB-byte rows at a pitch of RB + 16 bytes ----
 template <int RB>
-__device__ constexpr int swz(int row) {
-  static_assert(RB == 64 || RB == 128 || RB == 256, "tile rows are 64, 128 or 256 bytes");
-  constexpr int CPR = RB / 16;  // chunks per row; 16 / CPR rows share one 256-byte bank line
-  return (row / (16 / CPR)) % CPR;
+constexpr int pitch() {
+  static_assert(RB % 16 == 0 && RB >= 64 && RB <= 256, "tile rows of 64..256 bytes");
+  return RB + 16;
 }
+// 1 KB blocks a padded tile of ROWS rows occupies.
+template <int ROWS, int RB>
+constexpr int tile_blocks() { return (ROWS * pitch<RB>() + 1023) / 1024; }
 // Byte offset of byte `b` of row `row`.
 template <int RB>
-__device__ inline int tile_off(int row, int b) {
-  return row * RB + ((((b >> 4) ^ swz<RB>(row)) << 4) | (b & 15));
-}
+__device__ constexpr int tile_off(int row, int b) { return row * pitch<RB>() + b; }
 
 template <typename T> __device__ inline typename Mma<T>::frag lds_frag(const char* tile_base, int off);
 template <> __device__ inline bf16x8 lds_frag<bf16>(const char* p, int off) {
@@ -132,31 +135,136 @@ __device__ inline typename Mma<T>::frag tile_frag(const char* tile, int row, int
   return lds_frag<T>(tile, tile_off<RB>(row, e * (int)sizeof(T)));
 }
 
-// This wave's share of the direct-to-LDS copy of a tile of ROWS rows of RB bytes. Row r of
-// the tile is read from src + min(r, nvalid - 1) * ld bytes (rows past the valid range
-// repeat the last valid one; callers mask them). NW waves share the copy. `src` is the
-// same for the whole wave and the tile spans less than 4 GB, so each lane only carries a
-// 32-bit offset.
-template <int ROWS, int RB, int NW>
-__device__ inline void dma_tile(char* lds_tile, const char* src, uint32_t ld, int nvalid, int w, int lane) {
-  constexpr int BLOCKS = ROWS * RB / 1024;
-  static_assert(BLOCKS % NW == 0 || NW % BLOCKS == 0, "tile must split evenly over the waves");
-  constexpr int RPB = 1024 / RB;  // rows per 1 KB block
+// One direct-to-LDS copy: each lane moves 16 bytes from gptr to lds_block + 16 * lane
+// (lds_block is the same for the whole wave). It is issued as an opaque instruction: the
+// kernels order every copy themselves (explicit waits on the vector-memory counter, then a
+// barrier, before any wave reads the stage), and the compiler's own, coarser tracking of
+// such copies would otherwise wait for all of them before every LDS read.
+__device__ inline void dma16(const void* gptr, char* lds_block) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((LDS_PTR char*)lds_block));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr) : "memory", "m0");
+}
+
+// Global source of the 16 bytes that lane `lane` lands at byte 1024 b + 16 lane of a padded
+// tile whose row r is read from src + min(r, nvalid - 1) * ld (rows past the valid range
+// repeat the last valid one and are masked by the callers; pad slots and the slack after the
+// last row receive a valid chunk that is never read).
+template <int RB>
+__device__ inline const char* block_src(const char* src, uint32_t ld, int nvalid, int b, int lane) {
+  constexpr int P = pitch<RB>();
+  // The per-lane offsets are cheap to recompute; hiding the lane index from the optimiser
+  // keeps it from hoisting them out of the tile loop into registers the MFMA loop needs.
+  asm volatile("" : "+v"(lane));
+  const int byte = b * 1024 + lane * 16;
+  const int r = byte / P;
+  int o = byte - r * P;
+  o = o < RB ? o : 0;
+  const uint32_t sr = (uint32_t)min(r, nvalid - 1);
+  return src + (sr * ld + (uint32_t)o);
+}
+
+// A padded tile to copy: ROWS rows of RB bytes, row r read from src + min(r, nvalid - 1) * ld.
+template <int ROWS, int RB>
+struct TileSrc {
+  static constexpr int NB = tile_blocks<ROWS, RB>();
+  const char* src;
+  uint32_t ld;
+  int nvalid;
+};
+
+template <int OFF>
+__device__ __forceinline__ void dma_block_of(char*, int, int) {}
+template <int OFF, int ROWS, int RB, typename... Rest>
+__device__ __forceinline__ void dma_block_of(char* stage, int k, int lane, const TileSrc<ROWS, RB>& t,
+                                             const Rest&... rest) {
+  constexpr int NB = TileSrc<ROWS, RB>::NB;
+  if (k < OFF + NB) {
+    dma16(block_src<RB>(t.src, t.ld, t.nvalid, k - OFF, lane), stage + k * 1024);
+    return;
+  }
+  dma_block_of<OFF + NB>(stage, k, lane, rest...);
+}
+
+// 1 KB blocks of a stage made of the given tiles laid out back to back, and the copies each
+// of NW waves issues for it.
+template <typename... Tiles>
+constexpr int stage_blocks() { return (Tiles::NB + ...); }
+template <int NW, typename... Tiles>
+constexpr int stage_copies() { return (stage_blocks<Tiles...>() + NW - 1) / NW; }
+
+// This wave's share of the copies of one stage: blocks k = w + i * NW (i < stage_copies),
+// wrapping past the last block, so every wave issues the same count (two waves landing the
+// same block write identical bytes). w must be uniform across the wave.
+template <int NW, typename... Tiles>
+__device__ __forceinline__ void dma_stage(char* stage, int w, int lane, const Tiles&... tiles) {
+  constexpr int TOT = stage_blocks<Tiles...>();
 #pragma unroll
-  for (int i = 0; i < (BLOCKS + NW - 1) / NW; ++i) {
-    const int blk = w + i * NW;
-    if (BLOCKS < NW && blk >= BLOCKS) break;
-    const int row = blk * RPB + lane / (RB / 16);
-    const int pos = lane % (RB / 16);
-    const int chunk = pos ^ swz<RB>(row);
-    const uint32_t srow = (uint32_t)min(row, nvalid - 1);
-    const uint32_t off = srow * ld + (uint32_t)(chunk * 16);
-    __builtin_amdgcn_global_load_lds(src + off, (LDS_PTR void*)(lds_tile + blk * 1024), 16, 0, 0);
+  for (int i = 0; i < stage_copies<NW, Tiles...>(); ++i) {
+    int k = w + i * NW;
+    if (k >= TOT) k -= TOT * (k / TOT);
+    dma_block_of<0>(stage, k, lane, tiles...);
   }
 }
 
 // Waits for this wave's outstanding global loads, the direct-to-LDS copies included.
 __device__ inline void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Waits until at most N of this wave's vector-memory loads are outstanding (they complete
+// in issue order): vmcnt is bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] stay at
+// their maxima.
+template <int N>
+__device__ inline void wait_vm_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for the LDS pipelines: the caller has already waited for the copies and
+// LDS reads it needs, so no memory fence is attached (a fence would also wait for the copies
+// still in flight for later stages). The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ inline void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Calls f(integral_constant<S>) for S = 0 .. NS-1 (compile-time stage indices).
+template <int NS, int S = 0, typename F>
+__device__ __forceinline__ void for_stages(F&& f) {
+  if constexpr (S < NS) {
+    f(std::integral_constant<int, S>{});
+    for_stages<NS, S + 1>(f);
+  }
+}
+
+// Software pipeline over n >= 1 tiles and NS LDS stages: tile it lives in stage it % NS. At
+// the start of iteration it the copies of tile it + NS - 1 are issued; before the barrier
+// that ends iteration it, this wave's copies of tile it + 1 must have landed. DPT is the
+// number of copies one wave issues per tile. Past the last tile the free stage receives a
+// repeat of tile n - 1 (never read), so every iteration issues the same number of copies and
+// every wait is the same: at most (NS - 2) * DPT copies in flight. issue(it, stage) and
+// compute(it, stage) take the stage as an integral_constant so that each stage is its own
+// LDS object.
+template <int NS, int DPT, typename Issue, typename Compute>
+__device__ __forceinline__ void run_pipeline(int n, Issue&& issue, Compute&& compute) {
+  static_assert(NS >= 2 && (NS - 2) * DPT < 64, "pipeline depth");
+  wait_vm();  // the caller's own loads are done: inside, only copies count on vmcnt
+  for_stages<NS - 1>([&](auto S) { issue(min((int)S, n - 1), S); });
+  wait_vm_le<(NS - 2) * DPT>();
+  stage_barrier();
+  for (int base = 0; base < n; base += NS) {
+    for_stages<NS>([&](auto S) {
+      constexpr int st = decltype(S)::value;
+      const int it = base + st;
+      if (it >= n) return;
+      issue(min(it + NS - 1, n - 1), std::integral_constant<int, (st + NS - 1) % NS>{});
+      compute(it, S);
+      wait_vm_le<(NS - 2) * DPT>();
+      stage_barrier();
+    });
+  }
+  wait_vm();  // repeats still landing must finish before the workgroup's LDS is released
+}
 
 // ---- accumulator helpers ----
 // Elements s*E .. s*E+E-1 of an accumulator as an operand fragment (C map).

@@ -18,9 +18,22 @@ struct TransposeArgs {
   BranchTable seg;      // off: source row offsets; pad: column offsets; tile_prefix: pad/64
 };
 
+// ---- backward row statistics in transposed-copy column order (see statpack_kernel) ----
+struct StatPackArgs {
+  const float* lse;     // [H][rows]
+  const float* rowdot;  // [H][rows]
+  float* out;           // [2][H][cols]
+  int32_t H, rows;
+  int32_t row0;         // first row of segment 0 in lse/rowdot
+  int32_t cols;
+  int32_t nseg;
+  BranchTable seg;      // as for TransposeArgs
+};
+
 // ---- forward: query rows x HG heads per workgroup, 64-key LDS stages ----
 enum FwdMode { kFwdPrefill = 0, kFwdReplayPrompt = 1, kFwdReplayLocal = 2 };
 constexpr int kFwdBN = 64;   // keys per LDS stage
+constexpr int kFwdWaves = 8;  // waves per workgroup
 
 struct FwdArgs {
   const void* q;      // [nq_rows][Hq][D]
@@ -61,7 +74,7 @@ constexpr int kDkdvBM = 32;   // query rows per LDS stage
 struct DkdvArgs {
   const void* q; const void* dout;         // [nq_rows][Hq][D]
   const void* qt; const void* dot;         // transposed copies [Hq][D][qt_cols]
-  const float* lse; const float* rowdot;   // [Hq][nq_rows]
+  const float* stats;                      // [2][Hq][qt_cols]: lse * log2(e), rowdot (statpack)
   const void* k; const void* v;            // [nkv_rows][Hkv][D]
   void* dk; void* dv;                      // [nkv_rows][Hkv][D]: dtype, or float32 partials
   const float* init_dk; const float* init_dv;  // prefill: float32 [nkv][Hkv][D] added, or NULL
@@ -104,12 +117,13 @@ struct SplitReduceArgs {   // out[i] = sum_s part[s][i], s = 0..nsplit-1 in orde
   int32_t nsplit;
 };
 
-// Rows of one workgroup tile and heads per workgroup for a query-stationary kernel:
-// 4 waves of 32 rows; the waves of a workgroup cover hg query heads of one kv group.
+// Heads per workgroup of the query-stationary kernels (the waves of a workgroup cover that
+// many query heads of one kv group) and query rows per forward workgroup.
 int heads_per_wg(int group);
 int fwd_rows_per_wg(int group);
 
 hipError_t launch_transpose(int dtype, int D, const TransposeArgs& a, hipStream_t s);
+hipError_t launch_statpack(const StatPackArgs& a, hipStream_t s);
 hipError_t launch_attn_fwd(int dtype, int D, int mode, const FwdArgs& a, hipStream_t s);
 hipError_t launch_merge(int dtype, int D, const MergeArgs& a, hipStream_t s);
 hipError_t launch_rowdot(int dtype, int D, const RowDotArgs& a, hipStream_t s);

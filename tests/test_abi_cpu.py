@@ -58,11 +58,13 @@ def test_workspace_sizes():
     assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_PREFILL_FWD) == vp_t
     assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_PROMPT_FWD) == vp_t
     assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_LOCAL_FWD) == resp_kv_t
-    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_LOCAL_BWD) == 2 * resp_q_t
+    # row statistics in the same column order: [2][Hq][cols] float32
+    resp_st = 2 * Hq * 128 * 4
+    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_LOCAL_BWD) == 2 * resp_q_t + resp_st
     assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_DQ) == vp_t + resp_kv_t
-    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_PREFILL_KV_BWD) == 2 * Hq * D * 128 * 2
+    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_PREFILL_KV_BWD) == 2 * Hq * D * 128 * 2 + 2 * Hq * 128 * 4
     assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_PREFILL_DQ) == vp_t
-    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_PROMPT_BWD) >= 2 * resp_q_t
+    assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_PROMPT_BWD) >= 2 * resp_q_t + resp_st
     rf = _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_FWD)
     assert rf >= 2 * T * Hq * D * 4 + 2 * T * Hq * 4 + vp_t + resp_kv_t
     assert _lib.workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_BWD) >= T * Hq * 4 + 2 * resp_q_t + vp_t + resp_kv_t
