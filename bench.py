@@ -68,29 +68,64 @@ def stage_bytes(shape):
     }
 
 
-def cpu_baseline(w):
-    """The fp64 oracle on branch 0's flattened sequence (P + R_0 tokens) for query head 0,
-    forward + backward; extrapolated to the whole workload by flattened pair count x Hq
-    and converted to algorithmic TFLOP/s of the full workload."""
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The fp64 oracle, unmodified, on branch 0's flattened sequence (P + R_0 tokens), one
+    query head at a time (head h with its key/value head), forward + backward, until about
+    ``budget_s`` seconds of CPU work are done; extrapolated to the whole workload by
+    flattened pair count x Hq / heads done and converted to algorithmic TFLOP/s."""
     import torch
     from oracle import flattened_tree_attention
     from workloads import algorithmic_flops, pairs_flattened, make_shape
 
     s = w.shape
     R0 = s.lens[0]
+    group = s.Hq // s.Hkv
     sub = make_shape(s.P, [R0], 1, 1, s.D, dtype=s.dtype, std=s.std)
+    heads = 0
     t0 = time.perf_counter()
-    flattened_tree_attention(w.q_p[:, :1], w.k_p[:, :1], w.v_p[:, :1], w.q_r[:R0, :1], w.k_r[:R0, :1],
-                             w.v_r[:R0, :1], [0, R0], do_p=w.do_p[:, :1], do_r=w.do_r[:R0, :1])
+    while heads < s.Hq and (heads == 0 or time.perf_counter() - t0 < budget_s):
+        h, g = heads, heads // group
+        flattened_tree_attention(w.q_p[:, h:h + 1], w.k_p[:, g:g + 1], w.v_p[:, g:g + 1],
+                                 w.q_r[:R0, h:h + 1], w.k_r[:R0, g:g + 1], w.v_r[:R0, g:g + 1], [0, R0],
+                                 do_p=w.do_p[:, h:h + 1], do_r=w.do_r[:R0, h:h + 1])
+        heads += 1
     dt = time.perf_counter() - t0
-    sample_pairs = pairs_flattened(sub)
-    full_time = dt * (pairs_flattened(s) * s.Hq) / sample_pairs
+    factor = pairs_flattened(s) * s.Hq / (pairs_flattened(sub) * heads)
+    full_time = dt * factor
     value = algorithmic_flops(s) / full_time / 1e12
     return {"value": value, "unit": "TFLOP/s", "cores": torch.get_num_threads(), "kind": "oracle",
-            "sample": f"branch 0 flattened ({s.P}+{R0} tokens), query head 0, fwd+bwd in fp64: "
-                      f"{dt:.2f} s; extrapolated x{(pairs_flattened(s) * s.Hq) / sample_pairs:.1f} "
-                      f"(flattened pairs x Hq) to {full_time:.0f} s for the whole workload",
+            "sample": f"branch 0 flattened ({s.P}+{R0} tokens), query heads 0..{heads - 1}, fwd+bwd in "
+                      f"fp64: {dt:.2f} s; extrapolated x{factor:.1f} (flattened pairs x Hq / heads) to "
+                      f"{full_time:.0f} s for the whole workload",
             "sample_seconds": dt, "extrapolated_seconds": full_time}
+
+
+def kernel_source_digest():
+    """sha256 over the HIP sources, so stored counter readings are only reported for the
+    kernels they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "shared_prefix_attention_prompt_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(stage):
+    """HBM bytes per launch of ``stage`` from the committed counter runs, or None when they
+    were taken on other kernel sources or another workload."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get("stages", {}).get(stage)
+    if ent is None or rec.get("kernel_sources_sha256") != kernel_source_digest():
+        return None
+    return ent
 
 
 def main() -> int:
@@ -100,6 +135,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=4, help="workload number (1..5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed steps, run a plain elementwise copy of this many MiB "
+                         "three times (a known-size kernel to scale HBM byte counters by)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the shared-prefix "
@@ -215,9 +253,21 @@ def main() -> int:
         kernels[name] = entry
     dom = max(sf, key=lambda n: stage_ms[n])
     achieved = sf[dom] / (stage_ms[dom] / 1e3) / 1e12
+    tr_rec = stored_traffic(dom) if cfg == 4 else None
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": tr_rec["bytes_per_launch"] if tr_rec else None,
                 "alg_flops_per_launch": sf[dom], "avg_launch_ms": round(stage_ms[dom], 4)}
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline and s.backward:

@@ -253,10 +253,12 @@ int total_tiles(const BranchTable& bt) { return bt.tile_prefix[bt.G]; }
 char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 // ---- transposed copies ----
-// rows [r0, r0 + n) of x [rows][H][D] (one segment) -> [H][D][pad64(n)].
-augtree_status transpose_range(const Shape& s, const void* x, int H, int r0, int n, void* dst, hipStream_t st) {
+// rows [r0, r0 + n) of x [rows][H][D] (one segment) -> [H][pad64(n) / tw][D][tw].
+augtree_status transpose_range(const Shape& s, const void* x, int H, int r0, int n, int tw, void* dst,
+                               hipStream_t st) {
   TransposeArgs a;
   memset(&a, 0, sizeof(a));
+  a.tw = tw;
   a.src = static_cast<const char*>(x) + (size_t)r0 * H * s.D * s.esz();
   a.dst = dst;
   a.H = H;
@@ -273,10 +275,11 @@ augtree_status transpose_range(const Shape& s, const void* x, int H, int r0, int
   return AUGTREE_OK;
 }
 
-// all branches of x [T_R][H][D] -> [H][D][Tp], every branch padded to 64 columns.
-augtree_status transpose_branches(const Shape& s, const void* x, int H, void* dst, hipStream_t st) {
+// all branches of x [T_R][H][D] -> [H][Tp / tw][D][tw], every branch padded to 64 columns.
+augtree_status transpose_branches(const Shape& s, const void* x, int H, int tw, void* dst, hipStream_t st) {
   TransposeArgs a;
   memset(&a, 0, sizeof(a));
+  a.tw = tw;
   a.src = x;
   a.dst = dst;
   a.H = H;
@@ -566,7 +569,7 @@ augtree_status augtree_replay_prompt_fwd(const augtree_dims* dims, const void* k
   PTR(k_p); PTR(v_p); PTR(q_r); PTR(o_part); PTR(lse_part);
   CHECK(check_ws(ws, ws_bytes, op_workspace(s, AUGTREE_OP_REPLAY_PROMPT_FWD)));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  CHECK(transpose_range(s, v_p, s.Hkv, key_begin, key_end - key_begin, ws, st));
+  CHECK(transpose_range(s, v_p, s.Hkv, key_begin, key_end - key_begin, 64, ws, st));
   return step_replay_prompt_fwd(s, k_p, ws, q_r, key_begin, key_end, o_part, lse_part, st);
 }
 
@@ -578,7 +581,7 @@ augtree_status augtree_replay_local_fwd(const augtree_dims* dims, const void* q_
   PTR(q_r); PTR(k_r); PTR(v_r); PTR(o_part); PTR(lse_part);
   CHECK(check_ws(ws, ws_bytes, op_workspace(s, AUGTREE_OP_REPLAY_LOCAL_FWD)));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  CHECK(transpose_branches(s, v_r, s.Hkv, ws, st));
+  CHECK(transpose_branches(s, v_r, s.Hkv, 64, ws, st));
   return step_replay_local_fwd(s, q_r, k_r, ws, o_part, lse_part, st);
 }
 
@@ -622,8 +625,8 @@ augtree_status augtree_replay_prompt_bwd(const augtree_dims* dims, const void* k
   void* dort = at(ws, tr_resp(s, s.Hq));
   float* stats = reinterpret_cast<float*>(at(ws, 2 * tr_resp(s, s.Hq)));
   void* split = at(ws, 2 * tr_resp(s, s.Hq) + st_resp(s));
-  CHECK(transpose_branches(s, q_r, s.Hq, qrt, st));
-  CHECK(transpose_branches(s, do_r, s.Hq, dort, st));
+  CHECK(transpose_branches(s, q_r, s.Hq, 32, qrt, st));
+  CHECK(transpose_branches(s, do_r, s.Hq, 32, dort, st));
   CHECK(pack_stats_branches(s, lse_r, rowdot_r, stats, st));
   return step_replay_prompt_bwd(s, k_p, v_p, q_r, qrt, stats, do_r, dort, key_begin, key_end, dk_p_acc, dv_p_acc,
                                 split, st);
@@ -641,8 +644,8 @@ augtree_status augtree_replay_local_bwd(const augtree_dims* dims, const void* q_
   void* qrt = ws;
   void* dort = at(ws, tr_resp(s, s.Hq));
   float* stats = reinterpret_cast<float*>(at(ws, 2 * tr_resp(s, s.Hq)));
-  CHECK(transpose_branches(s, q_r, s.Hq, qrt, st));
-  CHECK(transpose_branches(s, do_r, s.Hq, dort, st));
+  CHECK(transpose_branches(s, q_r, s.Hq, 32, qrt, st));
+  CHECK(transpose_branches(s, do_r, s.Hq, 32, dort, st));
   CHECK(pack_stats_branches(s, lse_r, rowdot_r, stats, st));
   return step_replay_local_bwd(s, q_r, qrt, k_r, v_r, stats, do_r, dort, dk_r, dv_r, st);
 }
@@ -657,8 +660,8 @@ augtree_status augtree_replay_dq(const augtree_dims* dims, const void* k_p, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* kpt = ws;
   void* krt = at(ws, tr_prompt(s, s.Hkv));
-  CHECK(transpose_range(s, k_p, s.Hkv, 0, s.P, kpt, st));
-  CHECK(transpose_branches(s, k_r, s.Hkv, krt, st));
+  CHECK(transpose_range(s, k_p, s.Hkv, 0, s.P, 64, kpt, st));
+  CHECK(transpose_branches(s, k_r, s.Hkv, 64, krt, st));
   return step_replay_dq(s, k_p, kpt, v_p, q_r, k_r, krt, v_r, lse_r, rowdot_r, do_r, dq_r, st);
 }
 
@@ -678,8 +681,8 @@ augtree_status augtree_prefill_kv_bwd(const augtree_dims* dims, const void* q_p,
   void* qpt = ws;
   void* dopt = at(ws, tr_prompt(s, s.Hq));
   float* stats = reinterpret_cast<float*>(at(ws, 2 * tr_prompt(s, s.Hq)));
-  CHECK(transpose_range(s, q_p, s.Hq, 0, s.P, qpt, st));
-  CHECK(transpose_range(s, do_p, s.Hq, 0, s.P, dopt, st));
+  CHECK(transpose_range(s, q_p, s.Hq, 0, s.P, 32, qpt, st));
+  CHECK(transpose_range(s, do_p, s.Hq, 0, s.P, 32, dopt, st));
   CHECK(pack_stats_prompt(s, lse_p, rowdot_p, stats, st));
   return step_prefill_kv_bwd(s, q_p, qpt, k_p, v_p, stats, do_p, dopt, dk_p_acc, dv_p_acc, dk_p, dv_p, st);
 }
@@ -692,7 +695,7 @@ augtree_status augtree_prefill_dq(const augtree_dims* dims, const void* q_p, con
   PTR(q_p); PTR(k_p); PTR(v_p); PTR(lse_p); PTR(rowdot_p); PTR(do_p); PTR(dq_p);
   CHECK(check_ws(ws, ws_bytes, op_workspace(s, AUGTREE_OP_PREFILL_DQ)));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  CHECK(transpose_range(s, k_p, s.Hkv, 0, s.P, ws, st));
+  CHECK(transpose_range(s, k_p, s.Hkv, 0, s.P, 64, ws, st));
   return step_prefill_dq(s, q_p, k_p, ws, v_p, lse_p, rowdot_p, do_p, dq_p, st);
 }
 
@@ -706,7 +709,7 @@ augtree_status augtree_prefill_fwd(const augtree_dims* dims, const void* q_p, co
   PTR(q_p); PTR(k_p); PTR(v_p); PTR(o_p); PTR(lse_p);
   CHECK(check_ws(ws, ws_bytes, op_workspace(s, AUGTREE_OP_PREFILL_FWD)));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  CHECK(transpose_range(s, v_p, s.Hkv, 0, s.P, ws, st));
+  CHECK(transpose_range(s, v_p, s.Hkv, 0, s.P, 64, ws, st));
   return step_prefill_fwd(s, q_p, k_p, ws, o_p, lse_p, st);
 }
 
@@ -721,8 +724,8 @@ augtree_status augtree_replay_fwd(const augtree_dims* dims, const void* k_p, con
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* o_parts[2] = {reinterpret_cast<float*>(at(ws, w.o_a)), reinterpret_cast<float*>(at(ws, w.o_b))};
   float* l_parts[2] = {reinterpret_cast<float*>(at(ws, w.lse_a)), reinterpret_cast<float*>(at(ws, w.lse_b))};
-  CHECK(transpose_range(s, v_p, s.Hkv, 0, s.P, at(ws, w.vpt), st));
-  CHECK(transpose_branches(s, v_r, s.Hkv, at(ws, w.vrt), st));
+  CHECK(transpose_range(s, v_p, s.Hkv, 0, s.P, 64, at(ws, w.vpt), st));
+  CHECK(transpose_branches(s, v_r, s.Hkv, 64, at(ws, w.vrt), st));
   // (1) every branch row against the whole, unmasked prompt K/V: partial state a
   CHECK(step_replay_prompt_fwd(s, k_p, at(ws, w.vpt), q_r, 0, s.P, o_parts[0], l_parts[0], st));
   // (2) every branch row against its own branch, causally: partial state b
@@ -747,10 +750,10 @@ augtree_status augtree_replay_bwd(const augtree_dims* dims, const void* k_p, con
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* rowdot = reinterpret_cast<float*>(at(ws, w.rowdot));
   CHECK(step_row_dot(s, s.T, o_r, do_r, rowdot, st));
-  CHECK(transpose_branches(s, q_r, s.Hq, at(ws, w.qrt), st));
-  CHECK(transpose_branches(s, do_r, s.Hq, at(ws, w.dort), st));
-  CHECK(transpose_range(s, k_p, s.Hkv, 0, s.P, at(ws, w.kpt), st));
-  CHECK(transpose_branches(s, k_r, s.Hkv, at(ws, w.krt), st));
+  CHECK(transpose_branches(s, q_r, s.Hq, 32, at(ws, w.qrt), st));
+  CHECK(transpose_branches(s, do_r, s.Hq, 32, at(ws, w.dort), st));
+  CHECK(transpose_range(s, k_p, s.Hkv, 0, s.P, 64, at(ws, w.kpt), st));
+  CHECK(transpose_branches(s, k_r, s.Hkv, 64, at(ws, w.krt), st));
   float* stats = reinterpret_cast<float*>(at(ws, w.stats));
   CHECK(pack_stats_branches(s, lse_r, rowdot, stats, st));
   // prompt keys x all branches' rows (no mask): the branch sum of the prompt gradient
@@ -779,9 +782,9 @@ augtree_status augtree_prefill_bwd(const augtree_dims* dims, const void* q_p, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* rowdot = reinterpret_cast<float*>(at(ws, w.rowdot));
   CHECK(step_row_dot(s, s.P, o_p, do_p, rowdot, st));
-  CHECK(transpose_range(s, q_p, s.Hq, 0, s.P, at(ws, w.qpt), st));
-  CHECK(transpose_range(s, do_p, s.Hq, 0, s.P, at(ws, w.dopt), st));
-  CHECK(transpose_range(s, k_p, s.Hkv, 0, s.P, at(ws, w.kpt), st));
+  CHECK(transpose_range(s, q_p, s.Hq, 0, s.P, 32, at(ws, w.qpt), st));
+  CHECK(transpose_range(s, do_p, s.Hq, 0, s.P, 32, at(ws, w.dopt), st));
+  CHECK(transpose_range(s, k_p, s.Hkv, 0, s.P, 64, at(ws, w.kpt), st));
   float* stats = reinterpret_cast<float*>(at(ws, w.stats));
   CHECK(pack_stats_prompt(s, lse_p, rowdot, stats, st));
   CHECK(step_prefill_kv_bwd(s, q_p, at(ws, w.qpt), k_p, v_p, stats, do_p, at(ws, w.dopt), dk_p_acc, dv_p_acc, dk_p,

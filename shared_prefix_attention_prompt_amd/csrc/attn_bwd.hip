@@ -19,10 +19,15 @@
 //
 // Query tiles (dK/dV) and key tiles (dQ) are copied global -> LDS by direct loads through a
 // ring of LDS stages, both in natural layout and from the transposed copies (the operands of
-// the products that contract over the sequence).
+// the products that contract over the sequence; stored tile by tile, so each transposed LDS
+// tile is one contiguous block in memory).
 #include "kernels.hpp"
 
 namespace augtree {
+
+#ifndef DKDV_HOLD
+#define DKDV_HOLD false
+#endif
 
 template <typename T, typename OT, int D, int MODE>
 __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
@@ -90,7 +95,7 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
   }
 
   const uint32_t qld = (uint32_t)(a.Hq * D * ESZ);   // bytes between query rows
-  const uint32_t tld = (uint32_t)(a.qt_cols * ESZ);  // bytes between transposed rows
+  constexpr uint32_t tld = RBT;  // transposed tiles are contiguous [D][BM] blocks
   const int key = k0 + w * 32 + c;
   const bool kvalid = key < k1;
   const int wk_lo = k0 + w * 32;
@@ -138,11 +143,16 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
     return tl;
   };
 
+  CopyPlan<NW, DKDV_HOLD, TN, TN, TT, TT, TS> plan;
+  {
+    const uint32_t ld[5] = {qld, qld, tld, tld, (uint32_t)((int64_t)a.Hq * a.qt_cols * 4)};
+    plan.init(w, lane, ld);
+  }
   auto issue = [&](int it, auto S) {
     const Tile tl = tile_of(it);
     const int64_t nat = ((int64_t)tl.row0 * a.Hq + tl.hq) * D * ESZ;
-    const int64_t tr = ((int64_t)tl.hq * D * a.qt_cols + tl.col0) * ESZ;
-    dma_stage<NW>(stage(S), w, lane, TN{reinterpret_cast<const char*>(a.q) + nat, qld, tl.nval},
+    const int64_t tr = ((int64_t)tl.hq * a.qt_cols + tl.col0) * D * ESZ;  // tile-major copies
+    plan.issue(stage(S), lane, TN{reinterpret_cast<const char*>(a.q) + nat, qld, tl.nval},
                   TN{reinterpret_cast<const char*>(a.dout) + nat, qld, tl.nval},
                   TT{reinterpret_cast<const char*>(a.qt) + tr, tld, D},
                   TT{reinterpret_cast<const char*>(a.dot) + tr, tld, D},
@@ -319,8 +329,8 @@ __global__ __launch_bounds__(512, 2) void dq_kernel(DqArgs a) {
       nval = a.nprompt - kstart;
       kp = reinterpret_cast<const char*>(a.kp) + (int64_t)kstart * kld + (int64_t)kvh * D * ESZ;
       vp = reinterpret_cast<const char*>(a.vp) + (int64_t)kstart * kld + (int64_t)kvh * D * ESZ;
-      ktld = (uint32_t)(a.kpt_cols * ESZ);
-      ktp = reinterpret_cast<const char*>(a.kpt) + (int64_t)kvh * D * ktld + (int64_t)kstart * ESZ;
+      ktld = RBT;
+      ktp = reinterpret_cast<const char*>(a.kpt) + ((int64_t)kvh * a.kpt_cols + kstart) * D * ESZ;
       cz = false;
     } else {
       const int i = it - n0;
@@ -328,19 +338,24 @@ __global__ __launch_bounds__(512, 2) void dq_kernel(DqArgs a) {
       nval = kb1 - kstart;
       kp = reinterpret_cast<const char*>(a.k) + (int64_t)kstart * kld + (int64_t)kvh * D * ESZ;
       vp = reinterpret_cast<const char*>(a.v) + (int64_t)kstart * kld + (int64_t)kvh * D * ESZ;
-      ktld = (uint32_t)(a.kt_cols * ESZ);
-      ktp = reinterpret_cast<const char*>(a.kt) + (int64_t)kvh * D * ktld + (int64_t)(pcol0 + i * BN) * ESZ;
+      ktld = RBT;
+      ktp = reinterpret_cast<const char*>(a.kt) + ((int64_t)kvh * a.kt_cols + pcol0 + i * BN) * D * ESZ;
       cz = true;
     }
   };
 
+  CopyPlan<NW, true, TN, TN, TT> plan;
+  {
+    const uint32_t ld[3] = {kld, kld, (uint32_t)RBT};
+    plan.init(w, lane, ld);
+  }
   auto issue = [&](int it, auto S) {
     const char *kp, *vp, *ktp;
     uint32_t ktld;
     int ks, nv;
     bool cz;
     tile_src(it, kp, vp, ktp, ktld, ks, nv, cz);
-    dma_stage<NW>(stage(S), w, lane, TN{kp, kld, nv}, TN{vp, kld, nv}, TT{ktp, ktld, D});
+    plan.issue(stage(S), lane, TN{kp, kld, nv}, TN{vp, kld, nv}, TT{ktp, ktld, D});
   };
 
   auto compute = [&](int it, auto S) {

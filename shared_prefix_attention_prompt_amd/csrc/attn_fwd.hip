@@ -13,7 +13,8 @@
 //
 // Per wave and tile: S^T = K Q^T on the matrix cores, so the accumulator holds one query per
 // lane and the softmax statistics are per lane; P^T = exp2(S^T * scale*log2e - m) is fed
-// straight back as the B operand of O^T += V^T P^T, with V^T read from the transposed copy.
+// straight back as the B operand of O^T += V^T P^T, with V^T read from the transposed copy
+// (stored tile by tile, so each 64-key V^T tile is one contiguous block).
 // The running maximum is only raised when some row's tile maximum exceeds it by more than
 // 2^8 (in exp2 units); below that the stale maximum is kept, probabilities stay <= 2^8 and
 // the output accumulator is not rescaled. The result is the same softmax: the normaliser and
@@ -89,9 +90,9 @@ __global__ __launch_bounds__(kFwdWaves * 64, 2) void attn_fwd_kernel(FwdArgs a) 
   }
 
   const uint32_t kld = (uint32_t)(a.Hkv * D * ESZ);  // bytes between key rows
-  const uint32_t vld = (uint32_t)(a.vt_cols * ESZ);  // bytes between V^T rows
+  constexpr uint32_t vld = RBV;  // V^T tiles are contiguous [D][BN] blocks
   const char* kbase = reinterpret_cast<const char*>(a.k) + (int64_t)kvh * D * ESZ;
-  const char* vbase = reinterpret_cast<const char*>(a.vt) + (int64_t)kvh * D * a.vt_cols * ESZ;
+  const char* vbase = reinterpret_cast<const char*>(a.vt) + (int64_t)kvh * a.vt_cols * D * ESZ;
 
   const int wq0 = q0 + rb * 32;
   const int qrow = wq0 + c;
@@ -113,18 +114,23 @@ __global__ __launch_bounds__(kFwdWaves * 64, 2) void attn_fwd_kernel(FwdArgs a) 
   const float sl2 = a.scale_log2;
   const int nkt = (k1 - k0 + BN - 1) / BN;
 
+  CopyPlan<NW, true, TK, TV> plan;
+  {
+    const uint32_t ld[2] = {kld, vld};
+    plan.init(w, lane, ld);
+  }
   auto issue = [&](int it, auto S) {
     const int kt = k0 + it * BN;
-    dma_stage<NW>(stage(S), w, lane, TK{kbase + (int64_t)kt * kld, kld, k1 - kt},
-                  TV{vbase + (int64_t)(vcol0 + it * BN) * ESZ, vld, D});
+    plan.issue(stage(S), lane, TK{kbase + (int64_t)kt * kld, kld, k1 - kt},
+               TV{vbase + (int64_t)(vcol0 + it * BN) * D * ESZ, vld, D});
   };
 
-  auto compute = [&](int it, auto S) {
+  // Scores of tile it are computed one iteration early (while tile it - 1's softmax runs on
+  // the vector ALUs), into one of two register buffers chosen by the stage parity.
+  f32x16 sbuf[2][KB];
+  auto active = [&](int it) { return wave_has_rows && !(causal && k0 + it * BN > wq_hi); };
+  auto scores = [&](auto S, f32x16 (&sacc)[KB]) {
     const char* lk = stage(S);
-    const char* lv = lk + VOFF;
-    const int kt = k0 + it * BN;
-    if (!wave_has_rows || (causal && kt > wq_hi)) return;
-    f32x16 sacc[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       sacc[kb] = zero16();
@@ -132,6 +138,21 @@ __global__ __launch_bounds__(kFwdWaves * 64, 2) void attn_fwd_kernel(FwdArgs a) 
       for (int s = 0; s < KS; ++s)
         sacc[kb] = M::run(tile_frag<T, RBK>(lk, kb * 32 + c, s * M::K + g * M::E), qf[s], sacc[kb]);
     }
+  };
+
+  auto compute = [&](int it, auto S) {
+    constexpr int st = decltype(S)::value;
+    constexpr int nst = (st + 1) % NSTAGE;
+    static_assert(NSTAGE % 2 == 0, "buffer parity follows the stage");
+    f32x16 (&sacc)[KB] = sbuf[st & 1];
+    f32x16 (&snext)[KB] = sbuf[nst & 1];
+    if (it == 0) scores(S, sacc);
+    if (!active(it)) {
+      scores(std::integral_constant<int, nst>{}, snext);
+      return;
+    }
+    const char* lv = stage(S) + VOFF;
+    const int kt = k0 + it * BN;
     if ((kt + BN > k1) || (causal && kt + BN - 1 > wq0)) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -141,40 +162,66 @@ __global__ __launch_bounds__(kFwdWaves * 64, 2) void attn_fwd_kernel(FwdArgs a) 
           if (key >= k1 || (causal && key > qrow)) sacc[kb][r] = -kInf;
         }
     }
-    float mt = -kInf;
+    // The next tile's scores go to the matrix cores (its stage has landed; past the last
+    // tile it holds a repeat, whose scores are never used) interleaved, instruction by
+    // instruction, with this tile's maximum and probabilities (taken against the running
+    // maximum and redone in the rare case that it is raised). Scheduling barriers keep the
+    // order; K fragments are read two matrix ops ahead.
+    {
+      constexpr int NI = KB * KS;  // score matrix ops
+      constexpr int NE = KB * 16;  // softmax elements per lane
+      const char* lk = stage(std::integral_constant<int, nst>{});
+      auto kfrag = [&](int i) { return tile_frag<T, RBK>(lk, (i % KB) * 32 + c, (i / KB) * M::K + g * M::E); };
+      const float msc = m_run == -kInf ? 0.f : m_run * sl2;
+      typename M::frag fr[3];
+      fr[0] = kfrag(0);
+      fr[1] = kfrag(1);
+      float mt = -kInf;
+      f32x16 pacc[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int i = 0; i < NI; ++i) {
+        if (i + 2 < NI) fr[(i + 2) % 3] = kfrag(i + 2);
+        const int kb = i % KB, s_ = i / KB;
+        snext[kb] = M::run(fr[i % 3], qf[s_], s_ == 0 ? zero16() : snext[kb]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-    mt = halves_max(mt);
-    if (__builtin_amdgcn_ballot_w64(mt * sl2 > m_run * sl2 + kRescaleGap) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = m_new == -kInf ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * sl2);
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    const float msc = m_run == -kInf ? 0.f : m_run * sl2;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], sl2, -msc));
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const typename M::frag pf = acc_frag<T>(sacc[kb], s);
-        l_run = frag_sum(pf, l_run);
+        for (int j = i * NE / NI; j < (i + 1) * NE / NI; ++j) {
+          const float x = sacc[j / 16][j % 16];
+          mt = fmaxf(mt, x);
+          pacc[j / 16][j % 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, sl2, -msc));
+          asm volatile("" : "+v"(pacc[j / 16][j % 16]));  // computed here, not sunk into a branch
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mt = halves_max(mt);
+      if (__builtin_amdgcn_ballot_w64(mt * sl2 > m_run * sl2 + kRescaleGap) != 0) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = m_new == -kInf ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * sl2);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          oacc[db] = M::run(tile_frag<T, RBV>(lv, db * 32 + c, kb * 32 + tread<T>(s, g)), pf, oacc[db]);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+        const float msc2 = m_run == -kInf ? 0.f : m_run * sl2;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pacc[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], sl2, -msc2));
       }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const typename M::frag pf = acc_frag<T>(pacc[kb], s);
+          l_run = frag_sum(pf, l_run);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            oacc[db] = M::run(tile_frag<T, RBV>(lv, db * 32 + c, kb * 32 + tread<T>(s, g)), pf, oacc[db]);
+        }
+    }
   };
 
-  run_pipeline<NSTAGE, stage_copies<NW, TK, TV>()>(nkt, issue, compute);
+  run_pipeline<NSTAGE, stage_copies<NW, TK, TV>(), 1>(nkt, issue, compute);
 
   const float l = halves_sum(l_run);
   if (qvalid) {

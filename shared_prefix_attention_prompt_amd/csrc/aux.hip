@@ -5,10 +5,12 @@
 
 namespace augtree {
 
-// X [rows][H][D] -> X^T [H][D][cols]: one workgroup moves 64 sequence positions of one
-// segment (the prompt, a prompt key range, or one branch) and one head. Position i of the
-// segment lands in column pad[seg] + (i & ~15) + tpos(i & 15); the padding columns of a
-// segment's last tile are zero.
+// X [rows][H][D] -> X^T, tile-major: column col of head h, row d sits at
+// dst[((h * (cols / tw) + col / tw) * D + d) * tw + col % tw], so that one tw-column tile of
+// the consumer (all D rows) is a single contiguous block. One workgroup moves 64 sequence
+// positions of one segment (the prompt, a prompt key range, or one branch) and one head.
+// Position i of the segment lands in column pad[seg] + (i & ~15) + tpos(i & 15); the padding
+// columns of a segment's last tile are zero.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
   constexpr int PITCH = D + 4 / (int)sizeof(T);  // elements per LDS row: odd word stride
@@ -39,8 +41,9 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
       const int p = cc * EPC + e;
       out.e[e] = lds[((p & ~15) | tpos<T>(p & 15)) * PITCH + d];
     }
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(a.dst) +
-                              (((int64_t)h * D + d) * a.cols + col0 + cc * EPC) * sizeof(T)) = out.v;
+    const int col = col0 + cc * EPC;  // EPC consecutive columns never straddle a tile
+    const int64_t idx = (((int64_t)h * (a.cols / a.tw) + col / a.tw) * D + d) * a.tw + col % a.tw;
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(a.dst) + idx * sizeof(T)) = out.v;
   }
 }
 
@@ -163,6 +166,7 @@ hipError_t launch_statpack(const StatPackArgs& a, hipStream_t s) {
 
 hipError_t launch_transpose(int dtype, int D, const TransposeArgs& a, hipStream_t s) {
   if (a.cols == 0) return hipSuccess;
+  if ((a.tw != 32 && a.tw != 64) || a.cols % 64 != 0) return hipErrorInvalidValue;
   dim3 grid(a.cols / 64, a.H), block(256);
   if (dtype == 1 && D == 128) hipLaunchKernelGGL((transpose_kernel<bf16, 128>), grid, block, 0, s, a);
   else if (dtype == 1 && D == 64) hipLaunchKernelGGL((transpose_kernel<bf16, 64>), grid, block, 0, s, a);

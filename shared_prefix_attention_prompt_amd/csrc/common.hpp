@@ -18,7 +18,9 @@
 // transpose kernel: X^T[h][d][col] with the sequence index along col, permuted inside every
 // 16-column group by tpos() (bits 2 and 3 swapped, bf16) so that the 8 values one lane needs
 // are contiguous, and every segment (the prompt, or one branch) padded with zeros to a
-// multiple of 64 columns so that tiles never straddle segments.
+// multiple of 64 columns so that tiles never straddle segments. The copies are stored tile by
+// tile ([H][cols / tw][D][tw], tw = the consumer's tile width), so one LDS tile of a
+// transposed copy is a single contiguous block of memory.
 //
 // Tiles are copied from global memory into LDS by the direct-to-LDS load (each lane moves 16
 // bytes; the 64 lanes of one instruction fill 1 KB of LDS in lane order). A tile row of RB
@@ -30,6 +32,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
 #include <type_traits>
 
 namespace augtree {
@@ -164,8 +167,9 @@ __device__ inline const char* block_src(const char* src, uint32_t ld, int nvalid
 }
 
 // A padded tile to copy: ROWS rows of RB bytes, row r read from src + min(r, nvalid - 1) * ld.
-template <int ROWS, int RB>
+template <int ROWS_, int RB_>
 struct TileSrc {
+  static constexpr int ROWS = ROWS_, RB = RB_;
   static constexpr int NB = tile_blocks<ROWS, RB>();
   const char* src;
   uint32_t ld;
@@ -206,6 +210,134 @@ __device__ __forceinline__ void dma_stage(char* stage, int w, int lane, const Ti
   }
 }
 
+// ---- copy plans: the same copies, with per-lane offsets computed once per kernel ----
+// Block sizes and positions of a stage's tiles (compile time).
+template <typename... Tiles>
+struct StageLayout {
+  static constexpr int N = sizeof...(Tiles);
+  static constexpr int nb[N] = {Tiles::NB...};
+  static constexpr int TOT = (Tiles::NB + ...);
+  static constexpr int first(int t) {
+    int s = 0;
+    for (int i = 0; i < t; ++i) s += nb[i];
+    return s;
+  }
+  static constexpr int tile_of(int k) {
+    int t = 0;
+    while (t < N - 1 && k >= first(t + 1)) ++t;
+    return t;
+  }
+};
+
+// Direct copy from a wave-uniform base plus a per-lane 32-bit offset (the scalar-base form
+// of the load: no 64-bit address arithmetic per lane).
+__device__ inline void dma16_sbase(const char* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+
+template <int J, uint32_t MASK, int N>
+__device__ __forceinline__ const char* pick_base(int t, const char* const (&b)[N], const char* acc) {
+  if constexpr (J == N) {
+    return acc;
+  } else if constexpr (((MASK >> J) & 1u) == 0) {
+    return pick_base<J + 1, MASK>(t, b, acc);
+  } else if constexpr ((MASK & ((1u << J) - 1u)) == 0) {
+    return pick_base<J + 1, MASK>(t, b, b[J]);  // lowest candidate: the default
+  } else {
+    return pick_base<J + 1, MASK>(t, b, t == J ? b[J] : acc);
+  }
+}
+
+// The copies one wave issues per stage (blocks k = w + i * NW, wrapping, as dma_stage) with
+// the tile and LDS block of each fixed at kernel start. A stage whose tiles are all complete
+// (nvalid >= ROWS) is then issued with one scalar-base load per copy; a stage with a partial
+// tile falls back to dma_stage, which clamps rows per lane. HOLD: keep each copy's per-lane
+// source offset in a register (one per copy) or, where registers are short, recompute it
+// at every issue (a few integer operations per copy).
+template <int NW, bool HOLD, typename... Tiles>
+struct CopyPlan {
+  using L = StageLayout<Tiles...>;
+  static constexpr int N = L::N, TOT = L::TOT, DPT = (TOT + NW - 1) / NW;
+  static constexpr uint32_t cand(int i) {
+    uint32_t m = 0;
+    for (int w = 0; w < NW; ++w) m |= 1u << L::tile_of((w + i * NW) % TOT);
+    return m;
+  }
+  int w;
+  int tile[DPT];           // wave-uniform
+  int kofs[DPT];           // wave-uniform: LDS byte offset of the block in the stage
+  uint32_t off[HOLD ? DPT : 1];  // per lane (HOLD)
+  uint32_t ld[N];          // wave-uniform (recomputing plans)
+
+  template <int J = 0>
+  __device__ __forceinline__ static uint32_t lane_off(int t, int b, int lane, const uint32_t (&ld_)[N]) {
+    using TJ = std::tuple_element_t<J, std::tuple<Tiles...>>;
+    if constexpr (J + 1 < N) {
+      if (t != J) return lane_off<J + 1>(t, b, lane, ld_);
+    }
+    constexpr int P = pitch<TJ::RB>();
+    const int byte = b * 1024 + lane * 16;
+    const int r = min(byte / P, TJ::ROWS - 1);
+    int o = byte - (byte / P) * P;
+    o = o < TJ::RB ? o : 0;
+    return (uint32_t)r * ld_[J] + (uint32_t)o;
+  }
+
+  __device__ __forceinline__ int first_of(int t) const {
+    int f = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) f = t == j ? L::first(j) : f;
+    return f;
+  }
+
+  // ld_[t]: bytes between source rows of tile t.
+  __device__ __forceinline__ void init(int w_, int lane, const uint32_t (&ld_)[N]) {
+    w = w_;
+#pragma unroll
+    for (int j = 0; j < N; ++j) ld[j] = ld_[j];
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) {
+      const int k = (w + i * NW) % TOT;
+      int t = 0;
+#pragma unroll
+      for (int j = 1; j < N; ++j) t += k >= L::first(j) ? 1 : 0;
+      tile[i] = t;
+      kofs[i] = k * 1024;
+      if constexpr (HOLD) off[i] = lane_off(t, k - first_of(t), lane, ld_);
+    }
+  }
+
+  template <int I = 0>
+  __device__ __forceinline__ void issue_fast(uint32_t lds, int lane, const char* const (&b)[N]) const {
+    if constexpr (I < DPT) {
+      // slots that never wrap sit at w + I * NW blocks: one uniform base plus an immediate
+      const uint32_t k = (I * NW + NW - 1 < TOT) ? (uint32_t)(w * 1024 + I * NW * 1024) : (uint32_t)kofs[I];
+      uint32_t o;
+      if constexpr (HOLD) {
+        o = off[I];
+      } else {
+        // hidden from the optimiser, so that it is not hoisted out of the tile loop
+        asm volatile("" : "+v"(lane));
+        o = lane_off(tile[I], kofs[I] / 1024 - first_of(tile[I]), lane, ld);
+      }
+      dma16_sbase(pick_base<0, cand(I)>(tile[I], b, nullptr), o, lds + k);
+      issue_fast<I + 1>(lds, lane, b);
+    }
+  }
+
+  __device__ __forceinline__ void issue(char* stage, int lane, const Tiles&... tiles) const {
+    const bool full = ((tiles.nvalid >= Tiles::ROWS) && ...);
+    if (full) {
+      const char* const b[N] = {tiles.src...};
+      const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((LDS_PTR char*)stage));
+      issue_fast(lds, lane, b);
+    } else {
+      dma_stage<NW>(stage, w, lane, tiles...);
+    }
+  }
+};
+
 // Waits for this wave's outstanding global loads, the direct-to-LDS copies included.
 __device__ inline void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -239,18 +371,19 @@ __device__ __forceinline__ void for_stages(F&& f) {
 
 // Software pipeline over n >= 1 tiles and NS LDS stages: tile it lives in stage it % NS. At
 // the start of iteration it the copies of tile it + NS - 1 are issued; before the barrier
-// that ends iteration it, this wave's copies of tile it + 1 must have landed. DPT is the
+// that ends iteration it, this wave's copies of tiles up to it + 1 + LA must have landed, so
+// iteration it may read tiles it .. it + LA (LA: how far compute looks ahead). DPT is the
 // number of copies one wave issues per tile. Past the last tile the free stage receives a
 // repeat of tile n - 1 (never read), so every iteration issues the same number of copies and
-// every wait is the same: at most (NS - 2) * DPT copies in flight. issue(it, stage) and
+// every wait is the same: at most (NS - 2 - LA) * DPT copies in flight. issue(it, stage) and
 // compute(it, stage) take the stage as an integral_constant so that each stage is its own
 // LDS object.
-template <int NS, int DPT, typename Issue, typename Compute>
+template <int NS, int DPT, int LA = 0, typename Issue, typename Compute>
 __device__ __forceinline__ void run_pipeline(int n, Issue&& issue, Compute&& compute) {
-  static_assert(NS >= 2 && (NS - 2) * DPT < 64, "pipeline depth");
+  static_assert(NS >= 2 + LA && (NS - 2 - LA) * DPT < 64, "pipeline depth");
   wait_vm();  // the caller's own loads are done: inside, only copies count on vmcnt
   for_stages<NS - 1>([&](auto S) { issue(min((int)S, n - 1), S); });
-  wait_vm_le<(NS - 2) * DPT>();
+  wait_vm_le<(NS - 2 - LA) * DPT>();
   stage_barrier();
   for (int base = 0; base < n; base += NS) {
     for_stages<NS>([&](auto S) {
@@ -259,7 +392,7 @@ __device__ __forceinline__ void run_pipeline(int n, Issue&& issue, Compute&& com
       if (it >= n) return;
       issue(min(it + NS - 1, n - 1), std::integral_constant<int, (st + NS - 1) % NS>{});
       compute(it, S);
-      wait_vm_le<(NS - 2) * DPT>();
+      wait_vm_le<(NS - 2 - LA) * DPT>();
       stage_barrier();
     });
   }

@@ -8,12 +8,13 @@
 
 namespace augtree {
 
-// ---- transposed copies: X [rows][H][D] -> X^T [H][D][cols] (see common.hpp) ----
+// ---- transposed copies: X [rows][H][D] -> X^T, tile-major (see common.hpp) ----
 struct TransposeArgs {
   const void* src;      // [rows][H][D]
-  void* dst;            // [H][D][cols]
+  void* dst;            // [H][cols / tw][D][tw]
   int32_t H;
   int32_t cols;         // padded columns (multiple of 64)
+  int32_t tw;           // columns per tile (32 or 64): the consumer's LDS tile width
   int32_t nseg;         // segments: 1 (prompt or a prompt key range) or G (branches)
   BranchTable seg;      // off: source row offsets; pad: column offsets; tile_prefix: pad/64
 };
@@ -38,7 +39,7 @@ constexpr int kFwdWaves = 8;  // waves per workgroup
 struct FwdArgs {
   const void* q;      // [nq_rows][Hq][D]
   const void* k;      // [nkv_rows][Hkv][D]
-  const void* vt;     // transposed copy of V: [Hkv][D][vt_cols]
+  const void* vt;     // transposed copy of V, 64-column tiles: [Hkv][vt_cols / 64][D][64]
   void* o;            // [nq_rows][Hq][D], dtype (prefill) or float32 (replay partials)
   float* lse;         // [Hq][nq_rows]
   int32_t Hq, Hkv;
@@ -73,7 +74,7 @@ constexpr int kDkdvBM = 32;   // query rows per LDS stage
 
 struct DkdvArgs {
   const void* q; const void* dout;         // [nq_rows][Hq][D]
-  const void* qt; const void* dot;         // transposed copies [Hq][D][qt_cols]
+  const void* qt; const void* dot;         // transposed copies, 32-column tiles [Hq][qt_cols / 32][D][32]
   const float* stats;                      // [2][Hq][qt_cols]: lse * log2(e), rowdot (statpack)
   const void* k; const void* v;            // [nkv_rows][Hkv][D]
   void* dk; void* dv;                      // [nkv_rows][Hkv][D]: dtype, or float32 partials
@@ -98,7 +99,7 @@ struct DqArgs {
   const void* q; const void* dout;         // [nq_rows][Hq][D]
   const float* lse; const float* rowdot;   // [Hq][nq_rows]
   const void* k; const void* v;            // own keys: prompt (prefill) or response (response)
-  const void* kt;                          // transposed copy of own keys [Hkv][D][kt_cols]
+  const void* kt;                          // transposed own keys, 64-column tiles [Hkv][kt_cols / 64][D][64]
   const void* kp; const void* vp;          // response mode: the prompt keys/values
   const void* kpt;                         // response mode: transposed prompt keys
   void* dq;                                // [nq_rows][Hq][D]
