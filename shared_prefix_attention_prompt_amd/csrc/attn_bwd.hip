@@ -119,29 +119,50 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
   const int ntile = t_hi > t_lo ? t_hi - t_lo : 0;
   const int niter = ntile * group;
 
-  // Query tile of iteration it: head it / ntile, tile t_lo + it % ntile.
+  // Query tiles are walked head by head (the group's query heads in turn), tiles t_lo ..
+  // t_hi - 1 of each. The walk is a cursor advanced by one tile per issued stage (issue is
+  // called with consecutive iterations), so no iteration needs a division or a search of the
+  // branch table; the first row of each stage's tile is kept for the causal tests of compute.
   struct Tile { int hq, row0, col0, nval; };
-  auto tile_of = [&](int it) {
-    Tile tl;
-    tl.hq = kvh * group + it / ntile;
-    const int t = t_lo + it % ntile;
-    if constexpr (MODE == kDkdvPromptFromReplay) {
-      const int bb = branch_of_tile(a.bt, t);
-      const int j = t - a.bt.tile_prefix[bb];
-      tl.row0 = a.bt.off[bb] + j * BM;
-      tl.col0 = a.bt.pad[bb] + j * BM;
-      tl.nval = min(BM, a.bt.off[bb + 1] - tl.row0);
-    } else if constexpr (MODE == kDkdvLocal) {
-      tl.row0 = a.bt.off[b] + t * BM;
-      tl.col0 = a.bt.pad[b] + t * BM;
-      tl.nval = min(BM, a.bt.off[b + 1] - tl.row0);
-    } else {
-      tl.row0 = t * BM;
-      tl.col0 = t * BM;
-      tl.nval = min(BM, a.nq_rows - tl.row0);
-    }
-    return tl;
+  Tile cur{kvh * group, 0, 0, 0};
+  int cur_it = -1, cur_t = t_lo - 1;
+  // mode 0: the branch of cur_t: its first tile, row offset, column offset, end row, and the
+  // first tile of the next branch
+  int b_first = 0, b_row = 0, b_col = 0, b_end = 0, b_next = 0, bb = 0;
+  auto enter_branch = [&](int nb) {
+    bb = nb;
+    b_first = a.bt.tile_prefix[nb];
+    b_row = a.bt.off[nb];
+    b_col = a.bt.pad[nb];
+    b_end = a.bt.off[nb + 1];
+    b_next = a.bt.tile_prefix[nb + 1];
   };
+  auto advance = [&]() {
+    ++cur_it;
+    bool restart = cur_it == 0;
+    if (!restart && ++cur_t == t_hi) {
+      ++cur.hq;
+      restart = true;
+    }
+    if (restart) cur_t = t_lo;
+    if constexpr (MODE == kDkdvPromptFromReplay) {
+      if (restart) enter_branch(branch_of_tile(a.bt, cur_t));
+      else if (cur_t == b_next) enter_branch(bb + 1);
+      const int j = cur_t - b_first;
+      cur.row0 = b_row + j * BM;
+      cur.col0 = b_col + j * BM;
+      cur.nval = min(BM, b_end - cur.row0);
+    } else if constexpr (MODE == kDkdvLocal) {
+      cur.row0 = a.bt.off[b] + cur_t * BM;
+      cur.col0 = a.bt.pad[b] + cur_t * BM;
+      cur.nval = min(BM, a.bt.off[b + 1] - cur.row0);
+    } else {
+      cur.row0 = cur_t * BM;
+      cur.col0 = cur_t * BM;
+      cur.nval = min(BM, a.nq_rows - cur.row0);
+    }
+  };
+  int stage_row0[NSTAGE];
 
   CopyPlan<NW, DKDV_HOLD, TN, TN, TT, TT, TS> plan;
   {
@@ -149,7 +170,9 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
     plan.init(w, lane, ld);
   }
   auto issue = [&](int it, auto S) {
-    const Tile tl = tile_of(it);
+    if (cur_it < it) advance();
+    const Tile& tl = cur;
+    stage_row0[decltype(S)::value] = tl.row0;
     const int64_t nat = ((int64_t)tl.row0 * a.Hq + tl.hq) * D * ESZ;
     const int64_t tr = ((int64_t)tl.hq * a.qt_cols + tl.col0) * D * ESZ;  // tile-major copies
     plan.issue(stage(S), lane, TN{reinterpret_cast<const char*>(a.q) + nat, qld, tl.nval},
@@ -161,13 +184,12 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
   };
 
   auto compute = [&](int it, auto S) {
-    const Tile tl = tile_of(it);
     const char* q_ = stage(S);
     const char* o_ = q_ + O_DO;
     const char* qt_ = q_ + O_QT;
     const char* ot_ = q_ + O_DOT;
     const float* st = reinterpret_cast<const float*>(q_ + O_ST);
-    const int row0 = tl.row0;
+    const int row0 = stage_row0[decltype(S)::value];
     if (causal && row0 + 31 < wk_lo) return;  // every query of the tile precedes every key
     f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
