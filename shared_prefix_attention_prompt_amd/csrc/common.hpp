@@ -270,18 +270,31 @@ struct CopyPlan {
   uint32_t off[HOLD ? DPT : 1];  // per lane (HOLD)
   uint32_t ld[N];          // wave-uniform (recomputing plans)
 
-  template <int J = 0>
-  __device__ __forceinline__ static uint32_t lane_off(int t, int b, int lane, const uint32_t (&ld_)[N]) {
+  // Source offset of this lane's 16 bytes of block b of tile J (unsigned 24-bit arithmetic:
+  // row pitches of tiles with more than two rows are below 2^24 bytes; two-row tiles select).
+  template <int J>
+  __device__ __forceinline__ static uint32_t tile_lane_off(int b, int lane, uint32_t ld_) {
     using TJ = std::tuple_element_t<J, std::tuple<Tiles...>>;
-    if constexpr (J + 1 < N) {
-      if (t != J) return lane_off<J + 1>(t, b, lane, ld_);
+    constexpr uint32_t P = pitch<TJ::RB>();
+    const uint32_t byte = (uint32_t)b * 1024u + (uint32_t)lane * 16u;
+    const uint32_t q = byte / P;
+    const uint32_t r = q < (uint32_t)(TJ::ROWS - 1) ? q : (uint32_t)(TJ::ROWS - 1);
+    uint32_t o = byte - q * P;
+    o = o < (uint32_t)TJ::RB ? o : 0u;
+    if constexpr (TJ::ROWS <= 2) return (r != 0 ? ld_ : 0u) + o;
+    else return (r & 0xffffffu) * (ld_ & 0xffffffu) + o;
+  }
+  // The same for a tile t known to be one of the tiles in MASK (bit J: tile J).
+  template <uint32_t MASK, int J = 0>
+  __device__ __forceinline__ static uint32_t lane_off(int t, int b, int lane, const uint32_t (&ld_)[N]) {
+    if constexpr (((MASK >> J) & 1u) == 0) {
+      return lane_off<MASK, J + 1>(t, b, lane, ld_);
+    } else if constexpr ((MASK >> (J + 1)) == 0) {
+      return tile_lane_off<J>(b, lane, ld_[J]);  // the last candidate
+    } else {
+      if (t == J) return tile_lane_off<J>(b, lane, ld_[J]);
+      return lane_off<MASK, J + 1>(t, b, lane, ld_);
     }
-    constexpr int P = pitch<TJ::RB>();
-    const int byte = b * 1024 + lane * 16;
-    const int r = min(byte / P, TJ::ROWS - 1);
-    int o = byte - (byte / P) * P;
-    o = o < TJ::RB ? o : 0;
-    return (uint32_t)r * ld_[J] + (uint32_t)o;
   }
 
   __device__ __forceinline__ int first_of(int t) const {
@@ -291,21 +304,26 @@ struct CopyPlan {
     return f;
   }
 
+  template <int I = 0>
+  __device__ __forceinline__ void init_slots(int lane, const uint32_t (&ld_)[N]) {
+    if constexpr (I < DPT) {
+      const int k = (w + I * NW) % TOT;
+      int t = 0;
+#pragma unroll
+      for (int j = 1; j < N; ++j) t += k >= L::first(j) ? 1 : 0;
+      tile[I] = t;
+      kofs[I] = k * 1024;
+      if constexpr (HOLD) off[I] = lane_off<cand(I)>(t, k - first_of(t), lane, ld_);
+      init_slots<I + 1>(lane, ld_);
+    }
+  }
+
   // ld_[t]: bytes between source rows of tile t.
   __device__ __forceinline__ void init(int w_, int lane, const uint32_t (&ld_)[N]) {
     w = w_;
 #pragma unroll
     for (int j = 0; j < N; ++j) ld[j] = ld_[j];
-#pragma unroll
-    for (int i = 0; i < DPT; ++i) {
-      const int k = (w + i * NW) % TOT;
-      int t = 0;
-#pragma unroll
-      for (int j = 1; j < N; ++j) t += k >= L::first(j) ? 1 : 0;
-      tile[i] = t;
-      kofs[i] = k * 1024;
-      if constexpr (HOLD) off[i] = lane_off(t, k - first_of(t), lane, ld_);
-    }
+    init_slots(lane, ld_);
   }
 
   template <int I = 0>
@@ -319,7 +337,14 @@ struct CopyPlan {
       } else {
         // hidden from the optimiser, so that it is not hoisted out of the tile loop
         asm volatile("" : "+v"(lane));
-        o = lane_off(tile[I], kofs[I] / 1024 - first_of(tile[I]), lane, ld);
+        constexpr uint32_t C = cand(I);
+        if constexpr ((C & (C - 1)) == 0 && I * NW + NW - 1 < TOT) {
+          // a single candidate tile and no wrap: block w + I * NW - first of that tile
+          constexpr int J = __builtin_ctz(C);
+          o = tile_lane_off<J>(w + I * NW - L::first(J), lane, ld[J]);
+        } else {
+          o = lane_off<C>(tile[I], kofs[I] / 1024 - first_of(tile[I]), lane, ld);
+        }
       }
       dma16_sbase(pick_base<0, cand(I)>(tile[I], b, nullptr), o, lds + k);
       issue_fast<I + 1>(lds, lane, b);
