@@ -41,9 +41,10 @@
  * atomics are used anywhere; every reduction runs in a fixed order.
  *
  * Workspaces: every entry point that takes one writes transposed copies of some of its
- * operands there (head_dim-major, sequence-contiguous, each branch padded to 64 positions),
- * plus the partial results named at the entry point. augtree_workspace_bytes gives the size;
- * the pointer must be 256-byte aligned. The workspace holds nothing between calls.
+ * operands there (sequence-contiguous, each branch padded to 64 positions, stored tile by
+ * tile: one 32- or 64-position tile of all head_dim rows is one contiguous block), plus the
+ * partial results named at the entry point. augtree_workspace_bytes gives the size; the
+ * pointer must be 256-byte aligned. The workspace holds nothing between calls.
  */
 #ifndef AUGTREE_H
 #define AUGTREE_H
