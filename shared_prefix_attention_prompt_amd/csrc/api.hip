@@ -135,6 +135,35 @@ int prompt_split(const Shape& s, int nkeys) {
   return (int)n;
 }
 
+// Row-tile chunks of the prefill dK/dV walk. Unsplit (one workgroup per 256-key block and
+// kv head) when that already gives about two rounds of workgroups on 256 compute units; else
+// the fewest chunks (whole key blocks of rows each, at most 16) whose (key block, chunk)
+// units do. A key block only has units for the chunks holding rows it can see.
+struct PrefillSplit { int nz, zc, units; };
+PrefillSplit prefill_split(const Shape& s) {
+  const int nt = (s.P + kDkdvBM - 1) / kDkdvBM;
+  const int nk = (s.P + kDkdvKeysPerWG - 1) / kDkdvKeysPerWG;
+  constexpr int kTilesPerKeyBlock = kDkdvKeysPerWG / kDkdvBM;
+  PrefillSplit best{1, nt, nk};
+  if ((int64_t)nk * s.Hkv >= 512) return best;
+  for (int want = 2; want <= 16; ++want) {
+    const int per = (nt + want - 1) / want;
+    const int zc = (per + kTilesPerKeyBlock - 1) / kTilesPerKeyBlock * kTilesPerKeyBlock;
+    const int nz = (nt + zc - 1) / zc;
+    if (nz < 2 || nz <= best.nz) continue;
+    int units = 0;
+    for (int kb = 0; kb < nk; ++kb) units += nz - (kb * kTilesPerKeyBlock) / zc;
+    best = PrefillSplit{nz, zc, units};
+    if ((int64_t)units * s.Hkv >= 512) break;
+  }
+  return best;
+}
+
+size_t prefill_split_ws(const Shape& s) {
+  const PrefillSplit ps = prefill_split(s);
+  return ps.nz > 1 ? align_up((size_t)2 * ps.nz * s.P * s.Hkv * s.D * sizeof(float)) : 0;
+}
+
 // Float count of the split partials for a key range (split * keys * Hkv * D per tensor).
 size_t prompt_split_floats(const Shape& s, int nkeys) {
   const int n = prompt_split(s, nkeys);
@@ -194,7 +223,7 @@ ReplayBwdWs replay_bwd_ws(const Shape& s) {
   return w;
 }
 
-struct PrefillBwdWs { size_t rowdot, qpt, dopt, stats, kpt, total; };
+struct PrefillBwdWs { size_t rowdot, qpt, dopt, stats, kpt, split, total; };
 PrefillBwdWs prefill_bwd_ws(const Shape& s) {
   PrefillBwdWs w;
   Layout l;
@@ -203,6 +232,7 @@ PrefillBwdWs prefill_bwd_ws(const Shape& s) {
   w.dopt = l.add(tr_prompt(s, s.Hq));
   w.stats = l.add(st_prompt(s));
   w.kpt = l.add(tr_prompt(s, s.Hkv));
+  w.split = l.add(prefill_split_ws(s));
   w.total = l.total;
   return w;
 }
@@ -218,7 +248,7 @@ size_t op_workspace(const Shape& s, int op) {
     case AUGTREE_OP_REPLAY_LOCAL_FWD: return tr_resp(s, s.Hkv);
     case AUGTREE_OP_REPLAY_LOCAL_BWD: return 2 * tr_resp(s, s.Hq) + st_resp(s);
     case AUGTREE_OP_REPLAY_DQ: return tr_prompt(s, s.Hkv) + tr_resp(s, s.Hkv);
-    case AUGTREE_OP_PREFILL_KV_BWD: return 2 * tr_prompt(s, s.Hq) + st_prompt(s);
+    case AUGTREE_OP_PREFILL_KV_BWD: return 2 * tr_prompt(s, s.Hq) + st_prompt(s) + prefill_split_ws(s);
     case AUGTREE_OP_PREFILL_DQ: return tr_prompt(s, s.Hkv);
   }
   return 0;
@@ -479,23 +509,43 @@ augtree_status step_replay_dq(const Shape& s, const void* k_p, const void* kpt, 
   return AUGTREE_OK;
 }
 
+// split: chunk-partial workspace (prefill_split_ws bytes; unused when unsplit)
 augtree_status step_prefill_kv_bwd(const Shape& s, const void* q_p, const void* qpt, const void* k_p,
                                    const void* v_p, const float* stats, const void* do_p, const void* dopt,
                                    const float* dk_acc, const float* dv_acc, void* dk_p, void* dv_p,
-                                   hipStream_t st) {
+                                   void* split, hipStream_t st) {
+  const PrefillSplit ps = prefill_split(s);
+  const int64_t part = (int64_t)s.P * s.Hkv * s.D;
+  float* part_dk = static_cast<float*>(split);
+  float* part_dv = part_dk + (ps.nz > 1 ? (int64_t)ps.nz * part : 0);
   DkdvArgs p;
   memset(&p, 0, sizeof(p));
   p.q = q_p; p.dout = do_p; p.qt = qpt; p.dot = dopt; p.stats = stats;
-  p.k = k_p; p.v = v_p; p.dk = dk_p; p.dv = dv_p;
-  p.init_dk = dk_acc; p.init_dv = dv_acc;
+  p.k = k_p; p.v = v_p;
+  if (ps.nz > 1) {
+    p.dk = part_dk; p.dv = part_dv;  // float partials; the reduce adds dk_acc/dv_acc
+  } else {
+    p.dk = dk_p; p.dv = dv_p;
+    p.init_dk = dk_acc; p.init_dv = dv_acc;
+  }
   p.Hq = s.Hq; p.Hkv = s.Hkv;
   p.nq_rows = s.P; p.nkv_rows = s.P; p.qt_cols = pad64(s.P);
-  p.nktiles = (s.P + kDkdvKeysPerWG - 1) / kDkdvKeysPerWG;
-  p.nsplit = 1;
+  p.nktiles = ps.units;
+  p.nsplit = ps.nz;
+  p.zc = ps.zc;
+  p.split_stride = part;
   p.causal = 1;
-  p.nwg = p.nktiles * s.Hkv;
+  p.nwg = ps.units * s.Hkv;
   p.scale = s.scale; p.scale_log2 = s.scale * kLog2e;
   LAUNCH(launch_dkdv(s.dtype, s.D, kDkdvPrefill, p, st), "prefill dK/dV");
+  if (ps.nz > 1) {
+    PrefillReduceArgs r;
+    r.n = part; r.row_elems = s.Hkv * s.D; r.nz = ps.nz; r.zc = ps.zc;
+    r.part = part_dk; r.init = dk_acc; r.out = dk_p;
+    LAUNCH(launch_prefill_reduce(s.dtype, r, st), "prefill chunk reduce (dK)");
+    r.part = part_dv; r.init = dv_acc; r.out = dv_p;
+    LAUNCH(launch_prefill_reduce(s.dtype, r, st), "prefill chunk reduce (dV)");
+  }
   return AUGTREE_OK;
 }
 
@@ -684,7 +734,8 @@ augtree_status augtree_prefill_kv_bwd(const augtree_dims* dims, const void* q_p,
   CHECK(transpose_range(s, q_p, s.Hq, 0, s.P, 32, qpt, st));
   CHECK(transpose_range(s, do_p, s.Hq, 0, s.P, 32, dopt, st));
   CHECK(pack_stats_prompt(s, lse_p, rowdot_p, stats, st));
-  return step_prefill_kv_bwd(s, q_p, qpt, k_p, v_p, stats, do_p, dopt, dk_p_acc, dv_p_acc, dk_p, dv_p, st);
+  void* split = at(ws, 2 * tr_prompt(s, s.Hq) + st_prompt(s));
+  return step_prefill_kv_bwd(s, q_p, qpt, k_p, v_p, stats, do_p, dopt, dk_p_acc, dv_p_acc, dk_p, dv_p, split, st);
 }
 
 augtree_status augtree_prefill_dq(const augtree_dims* dims, const void* q_p, const void* k_p, const void* v_p,
@@ -788,7 +839,7 @@ augtree_status augtree_prefill_bwd(const augtree_dims* dims, const void* q_p, co
   float* stats = reinterpret_cast<float*>(at(ws, w.stats));
   CHECK(pack_stats_prompt(s, lse_p, rowdot, stats, st));
   CHECK(step_prefill_kv_bwd(s, q_p, at(ws, w.qpt), k_p, v_p, stats, do_p, at(ws, w.dopt), dk_p_acc, dv_p_acc, dk_p,
-                            dv_p, st));
+                            dv_p, at(ws, w.split), st));
   return step_prefill_dq(s, q_p, k_p, at(ws, w.kpt), v_p, lse_p, rowdot, do_p, dq_p, st);
 }
 

@@ -61,9 +61,10 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lid = xcd_remap(blockIdx.x, a.nwg);
-  const int per_kvh = a.nktiles * a.nsplit;
+  // workgroups per kv head: key tiles x splits (prompt walk), units (prefill chunks)
+  const int per_kvh = MODE == kDkdvPrefill ? a.nktiles : a.nktiles * a.nsplit;
   const int kvh = lid / per_kvh;
-  const int z = (lid % per_kvh) / a.nktiles;
+  int z = MODE == kDkdvPrefill ? 0 : (lid % per_kvh) / a.nktiles;
   const int kti = lid % a.nktiles;
   const int group = a.Hq / a.Hkv;
 
@@ -87,11 +88,28 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
     k1 = min(k0 + KPW, be);
     t_lo = (k0 - bs) / BM;
     t_hi = (be - bs + BM - 1) / BM;
-  } else {
+  } else if (a.nsplit == 1) {
     k0 = kti * KPW;
     k1 = min(k0 + KPW, a.nkv_rows);
     t_lo = k0 / BM;
     t_hi = (a.nq_rows + BM - 1) / BM;
+  } else {
+    // unit u of this kv head: key block kb and row-tile chunk z, key blocks in order, each
+    // with the chunks from the one holding its first visible row to the last
+    const int nt = (a.nq_rows + BM - 1) / BM;
+    int u = lid % a.nktiles, kb = 0;
+    for (;;) {
+      const int cnt = a.nsplit - (kb * (KPW / BM)) / a.zc;
+      if (u < cnt) break;
+      u -= cnt;
+      ++kb;
+    }
+    const int zz = (kb * (KPW / BM)) / a.zc + u;
+    z = zz;
+    k0 = kb * KPW;
+    k1 = min(k0 + KPW, a.nkv_rows);
+    t_lo = max(k0 / BM, zz * a.zc);
+    t_hi = min(nt, (zz + 1) * a.zc);
   }
 
   const uint32_t qld = (uint32_t)(a.Hq * D * ESZ);   // bytes between query rows
@@ -237,7 +255,7 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
 
   if (!kvalid) return;
   int64_t obase = ((int64_t)key * a.Hkv + kvh) * D;
-  if constexpr (MODE == kDkdvPromptFromReplay) obase += (int64_t)z * a.split_stride;
+  if constexpr (MODE != kDkdvLocal) obase += (int64_t)z * a.split_stride;  // split partials
   OT* dk = reinterpret_cast<OT*>(a.dk) + obase;
   OT* dv = reinterpret_cast<OT*>(a.dv) + obase;
 #pragma unroll
@@ -440,7 +458,10 @@ static hipError_t launch_dkdv_t(int mode, const DkdvArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((dkdv_kernel<T, float, D, kDkdvPromptFromReplay>), grid, block, 0, s, a);
       break;
     case kDkdvLocal: hipLaunchKernelGGL((dkdv_kernel<T, T, D, kDkdvLocal>), grid, block, 0, s, a); break;
-    case kDkdvPrefill: hipLaunchKernelGGL((dkdv_kernel<T, T, D, kDkdvPrefill>), grid, block, 0, s, a); break;
+    case kDkdvPrefill:
+      if (a.nsplit > 1) hipLaunchKernelGGL((dkdv_kernel<T, float, D, kDkdvPrefill>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((dkdv_kernel<T, T, D, kDkdvPrefill>), grid, block, 0, s, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

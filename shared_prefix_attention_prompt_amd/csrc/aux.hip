@@ -157,7 +157,34 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(SplitReduceArgs a) {
   *reinterpret_cast<f32x4*>(a.out + i4) = acc;
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillReduceArgs a) {
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i4 >= a.n) return;
+  const int key = (int)(i4 / a.row_elems);
+  const int zmin = (key / kDkdvKeysPerWG * 8) / a.zc;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int z = zmin; z < a.nz; ++z) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(a.part + z * a.n + i4);
+    acc[0] += x[0]; acc[1] += x[1]; acc[2] += x[2]; acc[3] += x[3];
+  }
+  if (a.init != nullptr) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(a.init + i4);
+    acc[0] += x[0]; acc[1] += x[1]; acc[2] += x[2]; acc[3] += x[3];
+  }
+  store4<T>(reinterpret_cast<T*>(a.out) + i4, acc[0], acc[1], acc[2], acc[3]);
+}
+
 // ---------------------------------------------------------------------------------------
+hipError_t launch_prefill_reduce(int dtype, const PrefillReduceArgs& a, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  if (a.n % 4 != 0 || a.row_elems % 4 != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((a.n / 4 + 255) / 256));
+  if (dtype == 1) hipLaunchKernelGGL(prefill_reduce_kernel<bf16>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(prefill_reduce_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_statpack(const StatPackArgs& a, hipStream_t s) {
   if (a.cols == 0) return hipSuccess;
   hipLaunchKernelGGL(statpack_kernel, dim3((a.cols + 255) / 256, a.H), dim3(256), 0, s, a);

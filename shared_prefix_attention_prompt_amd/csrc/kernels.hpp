@@ -81,9 +81,11 @@ struct DkdvArgs {
   const float* init_dk; const float* init_dv;  // prefill: float32 [nkv][Hkv][D] added, or NULL
   int32_t Hq, Hkv;
   int32_t nq_rows, nkv_rows, qt_cols;
-  int32_t nktiles;    // key tiles per kv head
+  int32_t nktiles;    // workgroups per kv head: key tiles (prefill split: key tile x chunk units)
   int32_t nqtiles;    // prompt-from-replay: query tiles (32-row tiles of every branch)
-  int32_t nsplit;     // prompt-from-replay: query tile range split count
+  int32_t nsplit;     // prompt-from-replay: query tile range split count; prefill: row-tile
+                      // chunks (1: unsplit; > 1: float partials per chunk, summed afterwards)
+  int32_t zc;         // prefill split: row tiles per chunk (a multiple of 8, whole key blocks)
   int32_t causal;     // 1: a key only sees queries at or after it (branch and prefill walks)
   int32_t nwg;
   int64_t split_stride;  // elements between split partial buffers
@@ -111,6 +113,18 @@ struct DqArgs {
   BranchTable bt;
 };
 
+// Prefill dK/dV from chunk partials: out[i] = (sum_{z >= zmin(key)} part[z][i]) + init[i],
+// z ascending, rounded once to the output type; zmin(key) = (key / 256 * 8) / zc is the
+// first chunk holding rows the key can see.
+struct PrefillReduceArgs {
+  const float* part;       // [nz][P][Hkv][D]
+  const float* init;       // [P][Hkv][D] or NULL
+  void* out;               // [P][Hkv][D] dtype
+  int64_t n;               // P * Hkv * D
+  int32_t row_elems;       // Hkv * D
+  int32_t nz, zc;
+};
+
 struct SplitReduceArgs {   // out[i] = sum_s part[s][i], s = 0..nsplit-1 in order
   const float* part;
   float* out;
@@ -131,6 +145,7 @@ hipError_t launch_rowdot(int dtype, int D, const RowDotArgs& a, hipStream_t s);
 hipError_t launch_dkdv(int dtype, int D, int mode, const DkdvArgs& a, hipStream_t s);
 hipError_t launch_dq(int dtype, int D, int mode, const DqArgs& a, hipStream_t s);
 hipError_t launch_split_reduce(const SplitReduceArgs& a, hipStream_t s);
+hipError_t launch_prefill_reduce(int dtype, const PrefillReduceArgs& a, hipStream_t s);
 
 constexpr int kDkdvKeysPerWG = 256;  // 8 waves x 32 keys
 

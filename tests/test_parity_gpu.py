@@ -57,6 +57,9 @@ def test_config1_fp32_full():
     (257, [200, 5], 8, 2, 128, "bf16"),
     (64, [128, 127, 2], 8, 1, 64, "bf16"),
     (300, [31, 33, 250, 1, 7], 4, 4, 128, "bf16"),
+    # prompts long enough for the prefill dK/dV walk to be split into row-tile chunks
+    (2050, [5, 9], 4, 1, 128, "bf16"),
+    (1100, [40, 300], 2, 2, 64, "bf16"),
 ])
 def test_small_trees(P, lens, Hq, Hkv, D, dtype):
     w = make_inputs(make_shape(P, lens, Hq, Hkv, D, dtype=dtype, std=1.0 if dtype == "f32" else 0.5),
