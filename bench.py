@@ -100,6 +100,38 @@ def cpu_baseline(w, budget_s: float = 12.0):
             "sample_seconds": dt, "extrapolated_seconds": full_time}
 
 
+def small_grid(shape):
+    """Whether the replay kernels' grids are too small to fill 256 compute units for long
+    (fewer than 8 rounds of the branch-row workgroups): then independent steps run on
+    separate streams, so one kernel's tail and idle units take another's workgroups."""
+    group = shape.Hq // shape.Hkv
+    hg = 4 if group % 4 == 0 else (2 if group % 2 == 0 else 1)
+    rows = 32 * 8 // hg
+    wgs = -(-shape.T // rows) * (shape.Hq // hg)
+    return wgs < 8 * 256
+
+
+def schedule(stages, nstreams):
+    """Issue plan: (kind, stream, name) with kind "run", "mark" (record an event) or "wait".
+    Three streams: the prompt prefill (and its row dot) beside the replay; the branch-local
+    forward beside the replay against the prompt; after the merge, the prompt K/V gradient
+    beside the branch K/V gradient and branch dQ; the prefill backward steps last on the two
+    busy streams. Every dependency of the path is an event; results are identical to the
+    one-stream order (no step's arithmetic depends on the schedule)."""
+    if nstreams == 1:
+        return [("run", 0, n) for n in stages]
+    p = [("run", 0, "prefill_fwd"), ("run", 2, "replay_local_fwd"), ("mark", 2, "f3"),
+         ("run", 1, "replay_prompt_fwd"), ("wait", 1, "f3"), ("run", 1, "merge")]
+    if "row_dot_r" not in stages:
+        return p
+    p += [("run", 0, "row_dot_p"), ("mark", 0, "rdp"),
+          ("run", 1, "row_dot_r"), ("mark", 1, "rdr"), ("run", 1, "replay_prompt_bwd"),
+          ("wait", 2, "rdr"), ("run", 2, "replay_local_bwd"), ("run", 2, "replay_dq"),
+          ("wait", 1, "rdp"), ("run", 1, "prefill_kv_bwd"),
+          ("wait", 2, "rdp"), ("run", 2, "prefill_dq")]
+    return p
+
+
 def kernel_source_digest():
     """sha256 over the HIP sources, so stored counter readings are only reported for the
     kernels they were taken on."""
@@ -135,6 +167,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=4, help="workload number (1..5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--streams", type=int, default=0, choices=[0, 1, 3],
+                    help="1: every step on one stream; 3: independent steps on three streams; "
+                         "0 (default): three when the kernels' grids are too small to fill the GPU")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run a plain elementwise copy of this many MiB "
                          "three times (a known-size kernel to scale HBM byte counters by)")
@@ -177,66 +212,89 @@ def main() -> int:
         "dv_p": torch.empty_like(t["v_p"]), "dq_p": torch.empty_like(t["q_p"]),
     }
     nws = max(_lib.workspace_bytes(tr.dims, op) for op in range(11))
-    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
+    main = torch.cuda.current_stream(dev)
+    nstreams = args.streams if args.streams > 0 else (3 if small_grid(s) else 1)
+    streams = [main] if nstreams == 1 else [torch.cuda.Stream(dev) for _ in range(3)]
+    wss = [torch.empty(max(nws, 256), dtype=torch.uint8, device=dev) for _ in streams]
+    b = buf
+    run = {
+        "prefill_fwd": lambda ws: _lib._check(_lib.augtree_prefill_fwd(
+            tr.dims, t["q_p"].data_ptr(), t["k_p"].data_ptr(), t["v_p"].data_ptr(), b["o_p"].data_ptr(),
+            b["lse_p"].data_ptr(), ws.data_ptr(), ws.numel(), tr.stream()), "augtree_prefill_fwd"),
+        "replay_prompt_fwd": lambda ws: ops.replay_prompt_fwd(tr, t["k_p"], t["v_p"], t["q_r"],
+                                                              out=(b["oa"], b["la"]), ws=ws),
+        "replay_local_fwd": lambda ws: ops.replay_local_fwd(tr, t["q_r"], t["k_r"], t["v_r"],
+                                                            out=(b["ob"], b["lb"]), ws=ws),
+        "merge": lambda ws: ops.merge_partials(tr, [(b["oa"], b["la"]), (b["ob"], b["lb"])],
+                                               out=(b["o_r"], b["lse_r"])),
+        "row_dot_r": lambda ws: ops.row_dot(tr, b["o_r"], t["do_r"], out=b["rd_r"]),
+        "replay_prompt_bwd": lambda ws: ops.replay_prompt_bwd(
+            tr, t["k_p"], t["v_p"], t["q_r"], b["lse_r"], b["rd_r"], t["do_r"], dk_acc=b["dk_acc"],
+            dv_acc=b["dv_acc"], ws=ws),
+        "replay_local_bwd": lambda ws: ops.replay_local_bwd(
+            tr, t["q_r"], t["k_r"], t["v_r"], b["lse_r"], b["rd_r"], t["do_r"], out=(b["dk_r"], b["dv_r"]), ws=ws),
+        "replay_dq": lambda ws: ops.replay_dq(tr, t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], b["lse_r"],
+                                              b["rd_r"], t["do_r"], out=b["dq_r"], ws=ws),
+        "row_dot_p": lambda ws: ops.row_dot(tr, b["o_p"], t["do_p"], out=b["rd_p"]),
+        "prefill_kv_bwd": lambda ws: ops.prefill_kv_bwd(
+            tr, t["q_p"], t["k_p"], t["v_p"], b["lse_p"], b["rd_p"], t["do_p"], b["dk_acc"], b["dv_acc"],
+            out=(b["dk_p"], b["dv_p"]), ws=ws),
+        "prefill_dq": lambda ws: ops.prefill_dq(tr, t["q_p"], t["k_p"], t["v_p"], b["lse_p"], b["rd_p"],
+                                                t["do_p"], out=b["dq_p"], ws=ws),
+    }
+    stages = STAGES if s.backward else STAGES[:4]
+    plan = schedule(stages, nstreams)
 
     def step(ev=None):
-        def mark(i):
-            if ev is not None:
-                ev[i].record(stream)
-        b = buf
-        mark(0)
-        _lib._check(_lib.augtree_prefill_fwd(tr.dims, t["q_p"].data_ptr(), t["k_p"].data_ptr(),
-                                             t["v_p"].data_ptr(), b["o_p"].data_ptr(), b["lse_p"].data_ptr(),
-                                             ws.data_ptr(), ws.numel(), tr.stream()), "augtree_prefill_fwd")
-        mark(1)
-        ops.replay_prompt_fwd(tr, t["k_p"], t["v_p"], t["q_r"], out=(b["oa"], b["la"]), ws=ws)
-        mark(2)
-        ops.replay_local_fwd(tr, t["q_r"], t["k_r"], t["v_r"], out=(b["ob"], b["lb"]), ws=ws)
-        mark(3)
-        ops.merge_partials(tr, [(b["oa"], b["la"]), (b["ob"], b["lb"])], out=(b["o_r"], b["lse_r"]))
-        mark(4)
-        if not s.backward:
-            return
-        ops.row_dot(tr, b["o_r"], t["do_r"], out=b["rd_r"])
-        mark(5)
-        ops.replay_prompt_bwd(tr, t["k_p"], t["v_p"], t["q_r"], b["lse_r"], b["rd_r"], t["do_r"],
-                              dk_acc=b["dk_acc"], dv_acc=b["dv_acc"], ws=ws)
-        mark(6)
-        ops.replay_local_bwd(tr, t["q_r"], t["k_r"], t["v_r"], b["lse_r"], b["rd_r"], t["do_r"],
-                             out=(b["dk_r"], b["dv_r"]), ws=ws)
-        mark(7)
-        ops.replay_dq(tr, t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], b["lse_r"], b["rd_r"], t["do_r"],
-                      out=b["dq_r"], ws=ws)
-        mark(8)
-        ops.row_dot(tr, b["o_p"], t["do_p"], out=b["rd_p"])
-        mark(9)
-        ops.prefill_kv_bwd(tr, t["q_p"], t["k_p"], t["v_p"], b["lse_p"], b["rd_p"], t["do_p"], b["dk_acc"],
-                           b["dv_acc"], out=(b["dk_p"], b["dv_p"]), ws=ws)
-        mark(10)
-        ops.prefill_dq(tr, t["q_p"], t["k_p"], t["v_p"], b["lse_p"], b["rd_p"], t["do_p"], out=b["dq_p"], ws=ws)
-        mark(11)
+        """One pass of the whole path. ev: per-stage (start, end) timing events, recorded on
+        the stream each stage runs on."""
+        if nstreams > 1:
+            fork = torch.cuda.Event()
+            fork.record(main)
+            for x in streams:
+                x.wait_event(fork)
+        marks = {}
+        for kind, si, name in plan:
+            st = streams[si]
+            if kind == "wait":
+                st.wait_event(marks[name])
+                continue
+            if kind == "mark":
+                marks[name] = torch.cuda.Event()
+                marks[name].record(st)
+                continue
+            with torch.cuda.stream(st):
+                if ev is not None:
+                    ev[name][0].record(st)
+                run[name](wss[si])
+                if ev is not None:
+                    ev[name][1].record(st)
+        if nstreams > 1:
+            for x in streams:
+                j = torch.cuda.Event()
+                j.record(x)
+                main.wait_event(j)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(args.steps)]
+    events = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in stages}
+              for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    start.record(stream)
+    start.record(main)
     for i in range(args.steps):
         step(events[i])
-    end.record(stream)
+    end.record(main)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = start.elapsed_time(end) / args.steps
 
-    stages = STAGES if s.backward else STAGES[:4]
     stage_ms = {}
-    for j, name in enumerate(stages):
-        stage_ms[name] = sum(events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)) / args.steps
+    for name in stages:
+        stage_ms[name] = sum(e[name][0].elapsed_time(e[name][1]) for e in events) / args.steps
     flops = algorithmic_flops(s)
     tflops = flops / (ms_per_step / 1e3) / 1e12
     peak = BF16_PEAK_TFLOPS if s.dtype == "bf16" else F32_PEAK_TFLOPS
@@ -282,7 +340,7 @@ def main() -> int:
         "config": {"workload": CONFIGS[cfg]["workload"], "P": s.P, "G": s.G, "branch_lens": list(s.lens),
                    "T_R": s.T, "Hq": s.Hq, "Hkv": s.Hkv, "D": s.D,
                    "passes": "fwd+bwd" if s.backward else "fwd",
-                   "alg_flops": flops, "seed": 20260000 + cfg},
+                   "alg_flops": flops, "seed": 20260000 + cfg, "streams": nstreams},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
         "wall_s": round(wall, 3),
     }
