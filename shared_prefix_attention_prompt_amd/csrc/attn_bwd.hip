@@ -26,7 +26,7 @@
 namespace augtree {
 
 #ifndef DKDV_HOLD
-#define DKDV_HOLD false
+#define DKDV_HOLD true
 #endif
 
 template <typename T, typename OT, int D, int MODE>
