@@ -418,15 +418,21 @@ __global__ __launch_bounds__(512, 2) void dq_kernel(DqArgs a) {
         sacc = M::run(tile_frag<T, RBN>(k_, kb * 32 + c, s * M::K + g * M::E), qf[s], sacc);
         pacc = M::run(tile_frag<T, RBN>(v_, kb * 32 + c, s * M::K + g * M::E), of[s], pacc);
       }
+      // the mask test is taken once per tile, not per element, so that the unmasked
+      // element loop is one straight block
+      auto softmax_grad = [&](auto masked) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], sl2, -lse2));
-        if (need_mask) {
-          const int kk = kt + kb * 32 + crow(r, g);
-          if (kk >= kend || (cz && kk > qrow)) p = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], sl2, -lse2));
+          if constexpr (decltype(masked)::value) {
+            const int kk = kt + kb * 32 + crow(r, g);
+            if (kk >= kend || (cz && kk > qrow)) p = 0.f;
+          }
+          pacc[r] = p * (pacc[r] - rdv);
         }
-        pacc[r] = p * (pacc[r] - rdv);
-      }
+      };
+      if (need_mask) softmax_grad(std::true_type{});
+      else softmax_grad(std::false_type{});
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const typename M::frag df = acc_frag<T>(pacc, s);
