@@ -205,6 +205,9 @@ __device__ __forceinline__ void dma_stage(char* stage, int w, int lane, const Ti
 #pragma unroll
   for (int i = 0; i < stage_copies<NW, Tiles...>(); ++i) {
     int k = w + i * NW;
+    // opaque here, so that the block tests are not hoisted out of a tile loop (into scalar
+    // registers the loop needs)
+    asm volatile("" : "+s"(k));
     if (k >= TOT) k -= TOT * (k / TOT);
     dma_block_of<0>(stage, k, lane, tiles...);
   }
