@@ -170,14 +170,20 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
       cur.row0 = b_row + j * BM;
       cur.col0 = b_col + j * BM;
       cur.nval = min(BM, b_end - cur.row0);
-    } else if constexpr (MODE == kDkdvLocal) {
-      cur.row0 = a.bt.off[b] + cur_t * BM;
-      cur.col0 = a.bt.pad[b] + cur_t * BM;
-      cur.nval = min(BM, a.bt.off[b + 1] - cur.row0);
     } else {
-      cur.row0 = cur_t * BM;
-      cur.col0 = cur_t * BM;
-      cur.nval = min(BM, a.nq_rows - cur.row0);
+      // causal walks run from the last row tile down to the key block's own, so the
+      // workgroups of one kv head (their key blocks start at different rows) walk the same
+      // rows at the same time and share them in L2
+      const int tt = t_lo + t_hi - 1 - cur_t;
+      if constexpr (MODE == kDkdvLocal) {
+        cur.row0 = a.bt.off[b] + tt * BM;
+        cur.col0 = a.bt.pad[b] + tt * BM;
+        cur.nval = min(BM, a.bt.off[b + 1] - cur.row0);
+      } else {
+        cur.row0 = tt * BM;
+        cur.col0 = tt * BM;
+        cur.nval = min(BM, a.nq_rows - cur.row0);
+      }
     }
   };
   int stage_row0[NSTAGE];
