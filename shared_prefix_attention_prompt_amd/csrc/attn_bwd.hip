@@ -10,9 +10,11 @@
 // the prompt keys this walk runs over all branches' rows at once, so the prompt gradient of
 // every branch is summed inside one accumulator ("Splitting Prompt Prefill from Response
 // Replay ...", §3.2: the prompt K/V gradient is the sum over branches) without atomics. When
-// the prompt has too few key tiles to fill the GPU, the query tiles are split into a fixed
-// number of parts whose fp32 partial sums are added afterwards in part order, so results
-// stay bitwise reproducible.
+// the keys alone cannot fill the GPU, the query tiles are split into a fixed number of parts
+// (the prompt walk over the branches) or row-tile chunks (the causal prefill walk) whose fp32
+// partial sums are added afterwards in a fixed order, so results stay bitwise reproducible.
+// Causal walks run from the last query tile down to the key block's own, so the workgroups of
+// one kv head, whose walks start at different rows, read the same rows at the same time.
 //
 // dQ is computed query-stationary in its own pass (it recomputes S and dP), which keeps it
 // free of atomics as well.
@@ -25,9 +27,6 @@
 
 namespace augtree {
 
-#ifndef DKDV_HOLD
-#define DKDV_HOLD true
-#endif
 
 template <typename T, typename OT, int D, int MODE>
 __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
@@ -188,7 +187,7 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
   };
   int stage_row0[NSTAGE];
 
-  CopyPlan<NW, DKDV_HOLD, TN, TN, TT, TT, TS> plan;
+  CopyPlan<NW, true, TN, TN, TT, TT, TS> plan;  // lane offsets held in registers
   {
     const uint32_t ld[5] = {qld, qld, tld, tld, (uint32_t)((int64_t)a.Hq * a.qt_cols * 4)};
     plan.init(w, lane, ld);

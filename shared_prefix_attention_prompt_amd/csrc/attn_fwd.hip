@@ -8,8 +8,9 @@
 //
 // A workgroup is 8 waves of 32 query rows (two per SIMD); its waves cover HG query heads of
 // one key/value group (HG = 4 for grouped-query heads, so one staged K/V tile serves four
-// heads). K/V tiles of 64 keys go global -> LDS by direct loads through a 4-stage ring: three
-// tiles are in flight while the current one is used.
+// heads). K/V tiles of 64 keys go global -> LDS by direct loads through a 4-stage ring: while
+// tile i is used, tile i + 1 is resident too (its scores are computed one iteration early,
+// interleaved with tile i's softmax) and two more are in flight.
 //
 // Per wave and tile: S^T = K Q^T on the matrix cores, so the accumulator holds one query per
 // lane and the softmax statistics are per lane; P^T = exp2(S^T * scale*log2e - m) is fed

@@ -1,6 +1,7 @@
 // Building blocks shared by the gfx950 attention kernels: matrix-core wrappers and the
-// 32x32 accumulator layout, direct global->LDS tile loads with an XOR-swizzled LDS layout,
-// the transposed operand layout, and small wave-level helpers.
+// 32x32 accumulator layout, the transposed operand layout, padded LDS tiles filled by direct
+// global->LDS copies (per-wave copy plans), the LDS stage pipeline, and small wave-level
+// helpers.
 //
 // Matrix-core conventions (one wave = 64 lanes, lane l: c = l & 31, g = l >> 5):
 //   A operand (M x K): lane holds row c and E consecutive "k slots" of half g.
