@@ -64,7 +64,9 @@ typedef enum { AUGTREE_F32 = 0, AUGTREE_BF16 = 1 } augtree_dtype;
 typedef enum {
   AUGTREE_OK = 0,
   AUGTREE_ERR_INVALID_ARGUMENT = 1, /* bad size, offsets, pointer or alignment */
-  AUGTREE_ERR_UNSUPPORTED = 2,      /* valid but not built: head_dim other than 64/128 */
+  AUGTREE_ERR_UNSUPPORTED = 2,      /* valid but not built: head_dim other than 64/128
+                                       (64 for float32), Hq*head_dim*element size >= 2^24
+                                       bytes per row, or a tensor beyond 2^31 elements */
   AUGTREE_ERR_WORKSPACE = 3,        /* workspace NULL or smaller than required */
   AUGTREE_ERR_HIP = 4               /* a HIP launch or runtime call failed */
 } augtree_status;

@@ -67,6 +67,11 @@ augtree_status check_dims(const augtree_dims* d, Shape* s) {
     return fail(AUGTREE_ERR_UNSUPPORTED, "bf16 head_dim %d not built (64 or 128)", d->head_dim);
   if (d->dtype == AUGTREE_F32 && d->head_dim != 64)
     return fail(AUGTREE_ERR_UNSUPPORTED, "f32 head_dim %d not built (64)", d->head_dim);
+  // the tile copies compute per-lane source offsets as row x row-pitch in 24-bit arithmetic
+  const int64_t pitch = (int64_t)d->num_q_heads * d->head_dim * (d->dtype == AUGTREE_BF16 ? 2 : 4);
+  if (pitch >= (int64_t)1 << 24)
+    return fail(AUGTREE_ERR_UNSUPPORTED, "num_q_heads x head_dim x element size = %lld bytes per row, "
+                "must be below 2^24", (long long)pitch);
   // every index of the kernels (elements of one tensor, rows x heads) stays in 32 bits
   const int64_t T = d->branch_offsets[d->num_branches];
   const int64_t rows = T > d->prompt_len ? T : d->prompt_len;

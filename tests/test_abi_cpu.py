@@ -48,7 +48,7 @@ def _dims(P=16, off=(0, 4, 9), Hq=4, Hkv=2, D=128, scale=0.088, dtype=_lib.AUGTR
 
 
 def test_workspace_sizes():
-    # transposed copies: [H][D][cols] bf16 with the prompt padded to 64 columns and every
+    # transposed copies: H x D x cols bf16 (stored tile by tile) with the prompt padded to 64 columns and every
     # branch padded to 64 columns on its own (30 -> 64, 40 -> 64)
     d, keep = _dims(P=100, off=(0, 30, 70), Hq=4, Hkv=2, D=128)
     T, P, Hq, Hkv, D = 70, 100, 4, 2, 128
@@ -90,6 +90,7 @@ FAKE = 1 << 20  # 16-byte aligned, never dereferenced: validation fails first
     (dict(scale=0.0), _lib.AUGTREE_ERR_INVALID_ARGUMENT, "softmax_scale"),
     (dict(scale=float("inf")), _lib.AUGTREE_ERR_INVALID_ARGUMENT, "softmax_scale"),
     (dict(dtype=5), _lib.AUGTREE_ERR_INVALID_ARGUMENT, "dtype"),
+    (dict(Hq=65536, Hkv=1), _lib.AUGTREE_ERR_UNSUPPORTED, "bytes per row"),
 ])
 def test_invalid_dims_are_rejected(kw, status, needle):
     d, keep = _dims(**kw)
