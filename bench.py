@@ -100,6 +100,28 @@ def cpu_baseline(w, budget_s: float = 12.0):
             "sample_seconds": dt, "extrapolated_seconds": full_time}
 
 
+def gemm_reference(dev, n=8192, reps=10):
+    """The vendor library's dense bf16 GEMM (torch.matmul of two contiguous n x n matrices)
+    timed right after the step: the matrix-core rate reachable at the clocks the chip runs at
+    under this load, as a yardstick beside the spec peak. Not part of the path."""
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(1)
+    a = torch.randn(n, n, generator=g).to(device=dev, dtype=torch.bfloat16).contiguous()
+    b = torch.randn(n, n, generator=g).to(device=dev, dtype=torch.bfloat16).contiguous()
+    c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return {"kind": f"torch.matmul bf16 {n}x{n}x{n}", "TFLOP/s": round(2 * n ** 3 / (ms / 1e3) / 1e12, 1)}
+
+
 def small_grid(shape):
     """Whether the replay kernels' grids are too small to fill 256 compute units for long
     (fewer than 8 rounds of the branch-row workgroups): then independent steps run on
@@ -170,6 +192,8 @@ def main() -> int:
     ap.add_argument("--streams", type=int, default=0, choices=[0, 1, 3],
                     help="1: every step on one stream; 3: independent steps on three streams; "
                          "0 (default): three when the kernels' grids are too small to fill the GPU")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip timing the vendor bf16 GEMM reported beside the roofline peak")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run a plain elementwise copy of this many MiB "
                          "three times (a known-size kernel to scale HBM byte counters by)")
@@ -316,6 +340,8 @@ def main() -> int:
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": tr_rec["bytes_per_launch"] if tr_rec else None,
                 "alg_flops_per_launch": sf[dom], "avg_launch_ms": round(stage_ms[dom], 4)}
+    if s.dtype == "bf16" and not args.no_gemm_reference:
+        roofline["gemm_reference"] = gemm_reference(dev)
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
