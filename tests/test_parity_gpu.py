@@ -60,6 +60,7 @@ def test_config1_fp32_full():
     # prompts long enough for the prefill dK/dV walk to be split into row-tile chunks
     (2050, [5, 9], 4, 1, 128, "bf16"),
     (1100, [40, 300], 2, 2, 64, "bf16"),
+    (600, [50, 70], 2, 1, 64, "f32"),
 ])
 def test_small_trees(P, lens, Hq, Hkv, D, dtype):
     w = make_inputs(make_shape(P, lens, Hq, Hkv, D, dtype=dtype, std=1.0 if dtype == "f32" else 0.5),
