@@ -61,6 +61,8 @@ def test_config1_fp32_full():
     (2050, [5, 9], 4, 1, 128, "bf16"),
     (1100, [40, 300], 2, 2, 64, "bf16"),
     (600, [50, 70], 2, 1, 64, "f32"),
+    # the most branches a tree may have (128), short and uneven
+    (33, [1 + (7 * i) % 23 for i in range(128)], 4, 2, 64, "bf16"),
 ])
 def test_small_trees(P, lens, Hq, Hkv, D, dtype):
     w = make_inputs(make_shape(P, lens, Hq, Hkv, D, dtype=dtype, std=1.0 if dtype == "f32" else 0.5),
