@@ -136,7 +136,9 @@ augtree_status augtree_replay_bwd(const augtree_dims *dims, const void *k_p, con
  *      attention backward)
  * out: dq_p [P][Hq][D], dk_p/dv_p [P][Hkv][D] = prompt queries' contribution + acc,
  *      rounded once to dtype.
- * Workspace: row statistics (Hq*P floats) and transposed Q/dO/K copies. */
+ * Workspace: row statistics, transposed Q/dO/K copies and, when the prompt dK/dV walk is
+ * cut into row chunks (prompts with few key tiles, or long prompts), the chunks' float32
+ * partial sums (2 * chunks * P*Hkv*D floats, at most 16 chunks). */
 augtree_status augtree_prefill_bwd(const augtree_dims *dims, const void *q_p, const void *k_p,
                                    const void *v_p, const void *o_p, const float *lse_p,
                                    const void *do_p, const float *dk_p_acc,

@@ -150,7 +150,21 @@ PrefillSplit prefill_split(const Shape& s) {
   const int nk = (s.P + kDkdvKeysPerWG - 1) / kDkdvKeysPerWG;
   constexpr int kTilesPerKeyBlock = kDkdvKeysPerWG / kDkdvBM;
   PrefillSplit best{1, nt, nk};
-  if ((int64_t)nk * s.Hkv >= 512) return best;
+  if ((int64_t)nk * s.Hkv >= 512) {
+    // Enough key blocks to fill the GPU. Long prompts are still cut into (at most 8) chunks of
+    // about kLockstepTiles row tiles: a key block's causal walk then starts at its chunk's end
+    // together with the other key blocks of that chunk instead of at the prompt's end at
+    // whatever time its workgroup starts, so the rows stay shared in L2.
+    constexpr int kLockstepTiles = 256;
+    if (nt < 2 * kLockstepTiles) return best;
+    const int want = std::min(8, nt / kLockstepTiles);
+    const int per = (nt + want - 1) / want;
+    const int zc = (per + kTilesPerKeyBlock - 1) / kTilesPerKeyBlock * kTilesPerKeyBlock;
+    const int nz = (nt + zc - 1) / zc;
+    int units = 0;
+    for (int kb = 0; kb < nk; ++kb) units += nz - (kb * kTilesPerKeyBlock) / zc;
+    return PrefillSplit{nz, zc, units};
+  }
   for (int want = 2; want <= 16; ++want) {
     const int per = (nt + want - 1) / want;
     const int zc = (per + kTilesPerKeyBlock - 1) / kTilesPerKeyBlock * kTilesPerKeyBlock;

@@ -93,17 +93,19 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
     t_lo = k0 / BM;
     t_hi = (a.nq_rows + BM - 1) / BM;
   } else {
-    // unit u of this kv head: key block kb and row-tile chunk z, key blocks in order, each
-    // with the chunks from the one holding its first visible row to the last
+    // unit u of this kv head: row-tile chunk z, the last chunk first, and inside it the key
+    // blocks that see the chunk (first row before its end), in order; the workgroups that run
+    // at the same time then walk the same rows of one chunk together and share them in L2
     const int nt = (a.nq_rows + BM - 1) / BM;
-    int u = lid % a.nktiles, kb = 0;
+    const int nk = (a.nkv_rows + KPW - 1) / KPW;
+    int u = lid % a.nktiles, zz = a.nsplit - 1;
     for (;;) {
-      const int cnt = a.nsplit - (kb * (KPW / BM)) / a.zc;
-      if (u < cnt) break;
+      const int cnt = min(nk, ((zz + 1) * a.zc + KPW / BM - 1) / (KPW / BM));
+      if (u < cnt || zz == 0) break;
       u -= cnt;
-      ++kb;
+      --zz;
     }
-    const int zz = (kb * (KPW / BM)) / a.zc + u;
+    const int kb = u;
     z = zz;
     k0 = kb * KPW;
     k1 = min(k0 + KPW, a.nkv_rows);
