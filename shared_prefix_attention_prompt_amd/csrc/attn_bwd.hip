@@ -11,7 +11,8 @@
 // every branch is summed inside one accumulator ("Splitting Prompt Prefill from Response
 // Replay ...", §3.2: the prompt K/V gradient is the sum over branches) without atomics. When
 // the keys alone cannot fill the GPU, the query tiles are split into a fixed number of parts
-// (the prompt walk over the branches) or row-tile chunks (the causal prefill walk) whose fp32
+// (the prompt walk over the branches) or row-tile chunks (the causal prefill walk; long
+// prompts are chunked too, so that concurrent workgroups walk the same rows) whose fp32
 // partial sums are added afterwards in a fixed order, so results stay bitwise reproducible.
 // Causal walks run from the last query tile down to the key block's own, so the workgroups of
 // one kv head, whose walks start at different rows, read the same rows at the same time.
