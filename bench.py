@@ -188,6 +188,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=4, help="workload number (1..5)")
+    ap.add_argument("--workload", default=None,
+                    help="a group-size / prompt:response-ratio sweep tree by name (group_g8, "
+                         "group_g16, group_g32, group_g64, response_heavy); overrides --config")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--streams", type=int, default=0, choices=[0, 1, 3],
                     help="1: every step on one stream; 3: independent steps on three streams; "
@@ -205,14 +208,17 @@ def main() -> int:
 
     import torch
     from shared_prefix_attention_prompt_amd import _lib, ops
-    from workloads import CONFIGS, algorithmic_flops, make_inputs
+    from workloads import SWEEPS, algorithmic_flops, config_seed, make_inputs, workload_name
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     _lib.load()
     dev = torch.device("cuda:0")
-    cfg = args.config
+    if args.workload is not None and args.workload not in SWEEPS:
+        print(f"unknown sweep tree {args.workload!r}; one of {sorted(SWEEPS)}", file=sys.stderr)
+        return 2
+    cfg = args.workload if args.workload is not None else args.config
     t_gen = time.perf_counter()
     w = make_inputs(cfg)
     s = w.shape
@@ -363,10 +369,10 @@ def main() -> int:
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": s.dtype,
         "data": "synthetic", "pct_bf16_peak": round(100 * tflops / peak, 2),
-        "config": {"workload": CONFIGS[cfg]["workload"], "P": s.P, "G": s.G, "branch_lens": list(s.lens),
+        "config": {"workload": workload_name(cfg), "P": s.P, "G": s.G, "branch_lens": list(s.lens),
                    "T_R": s.T, "Hq": s.Hq, "Hkv": s.Hkv, "D": s.D,
                    "passes": "fwd+bwd" if s.backward else "fwd",
-                   "alg_flops": flops, "seed": 20260000 + cfg, "streams": nstreams},
+                   "alg_flops": flops, "seed": config_seed(cfg), "streams": nstreams},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
         "wall_s": round(wall, 3),
     }

@@ -297,3 +297,28 @@ def test_generator_is_deterministic_and_follows_config_lengths():
     s3 = config_shape(3)
     assert s3.G == 8 and all(512 <= r <= 2048 for r in s3.lens)
     assert config_shape(3) == s3
+
+
+def test_sweep_trees_keep_the_token_budget_and_regimes():
+    # Group-size sweep: G in {8, 16, 32, 64} at a per-step budget G (L_P + L_R) of 256k tokens
+    # (in expectation; branch lengths are drawn around the target), 4:1 prompt:response; and
+    # one response-heavy tree. All on 28 query / 4 key-value heads, head_dim 128, bf16.
+    from workloads import SWEEPS, config_seed, config_shape, workload_name
+    seen = set()
+    for g in (8, 16, 32, 64):
+        name = f"group_g{g}"
+        s = config_shape(name)
+        assert s.G == g and (s.Hq, s.Hkv, s.D, s.dtype) == (28, 4, 128, "bf16")
+        budget = s.G * s.P + s.T
+        assert abs(budget - 262144) < 0.05 * 262144, (name, budget)
+        mean_r = s.T / s.G
+        assert 3.0 < s.P / mean_r < 5.5, (name, s.P, mean_r)
+        lo, hi = SWEEPS[name]["R"]
+        assert all(lo <= r <= hi for r in s.lens)
+        assert config_shape(name) == s
+        assert workload_name(name).startswith(f"group_g{g}_b256k")
+        seen.add(config_seed(name))
+    s = config_shape("response_heavy")
+    assert s.T / s.G > 3 * s.P
+    seen.add(config_seed("response_heavy"))
+    assert len(seen) == 5 and not seen & {config_seed(c) for c in range(1, 6)}

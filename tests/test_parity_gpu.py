@@ -153,6 +153,17 @@ def test_config5_sampled_rows_branch_grads_sum_rules():
     _sampled_check(5, n_prompt_rows=8, rows_per_branch=6, grad_branch_kv=7)
 
 
+# Group-size / prompt:response-ratio sweep trees at full size (28 query / 4 key-value heads):
+# sampled rows (first, middle and last row of every branch and a few random ones), the
+# smallest branch's own K/V gradients for one kv group, and the sum rules for all heads.
+@pytest.mark.parametrize("name,per_branch,kv", [("group_g8", 12, 0), ("group_g16", 8, 1),
+                                                ("group_g32", 4, 2), ("group_g64", 2, 3),
+                                                ("response_heavy", 12, 3)])
+def test_sweep_sampled_rows_branch_grads_sum_rules(name, per_branch, kv):
+    _sampled_check(name, n_prompt_rows=24, rows_per_branch=per_branch, grad_branch_kv=kv,
+                   sample_seed=len(name) * 100 + per_branch)
+
+
 def test_autograd_function_matches_entry_points():
     from shared_prefix_attention_prompt_amd import shared_prefix_attention
     w = make_inputs(make_shape(150, [40, 90], 4, 2, 128, dtype="bf16"), seed=5)

@@ -26,8 +26,8 @@ from typing import Dict, Optional, Sequence, Tuple
 
 import torch
 
-__all__ = ["Shape", "Workload", "CONFIGS", "config_shape", "make_inputs", "make_shape",
-           "config_seed", "pairs_reuse", "pairs_flattened", "algorithmic_flops"]
+__all__ = ["Shape", "Workload", "CONFIGS", "SWEEPS", "config_shape", "make_inputs", "make_shape",
+           "config_seed", "workload_name", "pairs_reuse", "pairs_flattened", "algorithmic_flops"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -97,7 +97,49 @@ CONFIGS: Dict[int, dict] = {
 }
 
 
-def config_seed(cfg: int) -> int:
+
+def _group_sweep_entry(G: int, budget: int = 262144, prompt_frac: float = 0.8) -> dict:
+    """One point of the group-size sweep: G branches whose flattened lengths P + R_i add up
+    to ``budget`` tokens in expectation (G (L_P + L_R) = budget), with a prompt share of
+    ``prompt_frac`` of each flattened sequence; R_i uniform in [L_R/2, 3 L_R/2]."""
+    per = budget // G
+    lr = int(round(per * (1.0 - prompt_frac)))
+    lp = per - lr
+    return dict(workload=f"group_g{G}_b{budget // 1024}k_p{lp}_r{lr // 2}-{3 * lr // 2}_gqa28-4_d128",
+                P=lp, G=G, R=(lr // 2, 3 * lr // 2), Hq=28, Hkv=4, D=128, dtype="bf16", std=0.5,
+                backward=True)
+
+
+# Group-size and prompt/response-ratio sweep ("Splitting Prompt Prefill from Response
+# Replay ...": §4.5 Fig. 18 varies G in {8, 16, 32, 64} at a fixed per-step token budget
+# G (L_P + L_R); §1 and §4.3 contrast prompt-heavy with response-heavy reasoning data). The
+# trees are synthetic stand-ins: a 256k-token budget (the paper's largest, §4.1) at a 4:1
+# prompt:response split for the group sizes, and a response-heavy tree (responses about 4x
+# the prompt). Every tree uses the attention layer of the paper's default model (28 query /
+# 4 key-value heads, head_dim 128, bf16; §4.1). Keyed by name; seeds 20260100 + index.
+SWEEPS: Dict[str, dict] = {}
+for _i, _g in enumerate((8, 16, 32, 64)):
+    SWEEPS[f"group_g{_g}"] = dict(_group_sweep_entry(_g), seed=20260101 + _i)
+SWEEPS["response_heavy"] = dict(
+    workload="response_heavy_p2048_g8xU6144-10240_gqa28-4_d128", P=2048, G=8, R=(6144, 10240),
+    Hq=28, Hkv=4, D=128, dtype="bf16", std=0.5, backward=True, seed=20260105)
+
+
+def _entry(cfg):
+    if isinstance(cfg, str) and cfg in SWEEPS:
+        return SWEEPS[cfg]
+    return CONFIGS[int(cfg)]
+
+
+def workload_name(cfg) -> str:
+    """Descriptive name (sizes) of numbered workload ``cfg`` or sweep tree ``cfg``."""
+    return _entry(cfg)["workload"]
+
+
+def config_seed(cfg) -> int:
+    """Seed of numbered workload ``cfg`` (20260000 + cfg) or of sweep tree ``cfg``."""
+    if isinstance(cfg, str) and cfg in SWEEPS:
+        return int(SWEEPS[cfg]["seed"])
     return 20260000 + int(cfg)
 
 
@@ -108,9 +150,9 @@ def _draw_lens(gen: torch.Generator, G: int, lo: int, hi: int) -> Tuple[int, ...
     return tuple(int(x) for x in r.tolist())
 
 
-def config_shape(cfg: int) -> Shape:
-    """Shape of numbered workload ``cfg`` with its seeded branch lengths."""
-    c = CONFIGS[cfg]
+def config_shape(cfg) -> Shape:
+    """Shape of numbered workload ``cfg`` (or sweep tree name) with its seeded branch lengths."""
+    c = _entry(cfg)
     gen = torch.Generator().manual_seed(config_seed(cfg))
     lens = _draw_lens(gen, c["G"], *c["R"])
     return Shape(P=c["P"], lens=lens, Hq=c["Hq"], Hkv=c["Hkv"], D=c["D"], dtype=c["dtype"],
@@ -133,13 +175,14 @@ def _randn(gen: torch.Generator, shape, std: float, dtype: torch.dtype) -> torch
 def make_inputs(shape_or_cfg, seed: Optional[int] = None) -> Workload:
     """Draw one workload.
 
-    ``shape_or_cfg`` is a config number (1..5) or a :class:`Shape`. For a config number the
-    seed defaults to ``config_seed(cfg)`` and the branch lengths are the first draw of that
-    same generator, so ``make_inputs(cfg)`` is fully determined by ``cfg``.
+    ``shape_or_cfg`` is a config number (1..5), a sweep tree name (``SWEEPS``) or a
+    :class:`Shape`. For a number or name the seed defaults to ``config_seed(cfg)`` and the
+    branch lengths are the first draw of that same generator, so ``make_inputs(cfg)`` is fully
+    determined by ``cfg``.
     """
-    if isinstance(shape_or_cfg, int):
+    if isinstance(shape_or_cfg, (int, str)):
         cfg = shape_or_cfg
-        c = CONFIGS[cfg]
+        c = _entry(cfg)
         gen = torch.Generator().manual_seed(config_seed(cfg) if seed is None else seed)
         lens = _draw_lens(gen, c["G"], *c["R"])
         shape = Shape(P=c["P"], lens=lens, Hq=c["Hq"], Hkv=c["Hkv"], D=c["D"],
