@@ -125,19 +125,34 @@ size_t tr_resp(const Shape& s, int H) { return tr_bytes(s, H, s.Tp()); }
 size_t st_prompt(const Shape& s) { return align_up((size_t)2 * s.Hq * pad64(s.P) * sizeof(float)); }
 size_t st_resp(const Shape& s) { return align_up((size_t)2 * s.Hq * s.Tp() * sizeof(float)); }
 
-// Split count of the prompt dK/dV pass over the branches' rows for `nkeys` prompt keys:
-// enough workgroups (one per compute unit at a time) for about two rounds on 256 compute
-// units, never more parts than query tiles, at most 16.
+// Split count of the prompt dK/dV pass over the branches' rows for `nkeys` prompt keys. One
+// workgroup runs per compute unit at a time (LDS-bound), so a grid of W workgroups takes
+// ceil(W / 256) rounds; a fractional last round leaves units idle. Among n = 1..16 parts
+// (never more than the query tiles) giving at least two rounds of workgroups where that is
+// possible, the count with the least modelled time is taken: ceil(wgs n / 256) rounds of
+// T_R / n rows each, plus writing and re-reading the n float32 partial sums (two tensors of
+// nkeys x Hkv x D, at about 5 TB/s against about 4.3 TFLOP/s per compute unit on the
+// products, i.e. nkeys * Hkv * 0.0067 / group row-walks per part).
 int prompt_split(const Shape& s, int nkeys) {
   const int64_t wgs = (int64_t)((nkeys + kDkdvKeysPerWG - 1) / kDkdvKeysPerWG) * s.Hkv;
-  const int64_t target = 512;
-  int64_t n = (target + wgs - 1) / wgs;
   int64_t qtiles = 0;
   for (int i = 0; i < s.G; ++i) qtiles += (s.off[i + 1] - s.off[i] + kDkdvBM - 1) / kDkdvBM;
-  if (n > qtiles) n = qtiles;
-  if (n > 16) n = 16;
-  if (n < 1) n = 1;
-  return (int)n;
+  const int64_t nmax = std::max<int64_t>(1, std::min<int64_t>(16, qtiles));
+  const double reduce = (double)nkeys * s.Hkv * 0.0067 / (s.Hq / s.Hkv);
+  int best = 1;
+  double best_cost = 0.0;
+  bool best_fills = false;
+  for (int64_t n = 1; n <= nmax; ++n) {
+    const int64_t w = wgs * n;
+    const bool fills = w >= 512 || n == nmax;
+    const double cost = (double)((w + 255) / 256) * (double)((s.T + n - 1) / n) + (n > 1 ? (double)n * reduce : 0.0);
+    if (n == 1 || (fills && !best_fills) || (fills == best_fills && cost < best_cost)) {
+      best = (int)n;
+      best_cost = cost;
+      best_fills = fills;
+    }
+  }
+  return best;
 }
 
 // Row-tile chunks of the prefill dK/dV walk. Unsplit (one workgroup per 256-key block and
@@ -198,7 +213,6 @@ size_t prompt_split_ws(const Shape& s) {
     const int nk = t == nkt ? s.P : t * kDkdvKeysPerWG;
     const size_t f = prompt_split_floats(s, nk);
     if (f > best) best = f;
-    if (prompt_split(s, nk) == 1) break;  // larger ranges do not split
   }
   return align_up(2 * best * sizeof(float));
 }
