@@ -180,15 +180,36 @@ PrefillSplit prefill_split(const Shape& s) {
     for (int kb = 0; kb < nk; ++kb) units += nz - (kb * kTilesPerKeyBlock) / zc;
     return PrefillSplit{nz, zc, units};
   }
-  for (int want = 2; want <= 16; ++want) {
+  // Too few key blocks to fill the GPU: the fewest-cost chunk count. Units are uneven (a key
+  // block sees only the rows after it), so the pass takes about the average work per compute
+  // unit plus half the longest unit; each chunk adds its float32 partial sums (written once,
+  // read once by the reduce, at about 5 TB/s). Times in row-tile walks of one workgroup
+  // (32 rows x 256 keys per query head, about 2 us at the measured matrix rate).
+  const int group = s.Hq / s.Hkv;
+  const double tile_us = 1.95 * group;
+  double best_cost = 1e300;
+  for (int want = 1; want <= 16; ++want) {
     const int per = (nt + want - 1) / want;
     const int zc = (per + kTilesPerKeyBlock - 1) / kTilesPerKeyBlock * kTilesPerKeyBlock;
     const int nz = (nt + zc - 1) / zc;
-    if (nz < 2 || nz <= best.nz) continue;
+    if (want > 1 && nz <= best.nz) continue;
     int units = 0;
-    for (int kb = 0; kb < nk; ++kb) units += nz - (kb * kTilesPerKeyBlock) / zc;
-    best = PrefillSplit{nz, zc, units};
-    if ((int64_t)units * s.Hkv >= 512) break;
+    int64_t tiles = 0;
+    int longest = 0;
+    for (int kb = 0; kb < nk; ++kb) {
+      for (int z = (kb * kTilesPerKeyBlock) / zc; z < nz; ++z) {
+        const int len = std::min(nt, (z + 1) * zc) - std::max(kb * kTilesPerKeyBlock, z * zc);
+        ++units;
+        tiles += len;
+        longest = std::max(longest, len);
+      }
+    }
+    const double pass = ((double)tiles * s.Hkv / 256.0 + 0.5 * longest) * tile_us;
+    const double partial = nz > 1 ? (double)nz * s.P * s.Hkv * s.D * 16.0 / 5e6 : 0.0;
+    if (pass + partial < best_cost) {
+      best_cost = pass + partial;
+      best = PrefillSplit{nz, nz > 1 ? zc : nt, units};
+    }
   }
   return best;
 }
