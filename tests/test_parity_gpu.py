@@ -61,6 +61,10 @@ def test_config1_fp32_full():
     (2050, [5, 9], 4, 1, 128, "bf16"),
     (1100, [40, 300], 2, 2, 64, "bf16"),
     (600, [50, 70], 2, 1, 64, "f32"),
+    # short prompts with few kv heads: the prompt K/V gradient over the branches is split 16
+    # ways and the prefill walk cut into 6 and 12 row-tile chunks
+    (1500, [300, 200, 417], 4, 1, 128, "bf16"),
+    (3000, [700, 45, 1210], 8, 2, 128, "bf16"),
     # the most branches a tree may have (128), short and uneven
     (33, [1 + (7 * i) % 23 for i in range(128)], 4, 2, 64, "bf16"),
 ])
