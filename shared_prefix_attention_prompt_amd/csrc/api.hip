@@ -155,10 +155,11 @@ int prompt_split(const Shape& s, int nkeys) {
   return best;
 }
 
-// Row-tile chunks of the prefill dK/dV walk. Unsplit (one workgroup per 256-key block and
-// kv head) when that already gives about two rounds of workgroups on 256 compute units; else
-// the fewest chunks (whole key blocks of rows each, at most 16) whose (key block, chunk)
-// units do. A key block only has units for the chunks holding rows it can see.
+// Row-tile chunks of the prefill dK/dV walk. When the key blocks fill the GPU (about two
+// rounds of one-per-CU workgroups), long prompts are cut into chunks of about 8192 rows so that
+// concurrent walks share rows in L2; otherwise the chunk count (whole key blocks of rows each,
+// at most 16) is the one with the least modelled time. A key block only has units for the
+// chunks holding rows it can see.
 struct PrefillSplit { int nz, zc, units; };
 PrefillSplit prefill_split(const Shape& s) {
   const int nt = (s.P + kDkdvBM - 1) / kDkdvBM;
