@@ -11,3 +11,4 @@ tree mask, finite differences, and invariants of the mathematics).
 """
 from .flat_attention import (rows_attention, flattened_tree_attention,  # noqa: F401
                              flattened_sampled_rows, branch_response_grads)
+from .flat_chain import flattened_chain  # noqa: F401

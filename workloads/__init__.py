@@ -27,7 +27,8 @@ from typing import Dict, Optional, Sequence, Tuple
 import torch
 
 __all__ = ["Shape", "Workload", "CONFIGS", "SWEEPS", "config_shape", "make_inputs", "make_shape",
-           "config_seed", "workload_name", "pairs_reuse", "pairs_flattened", "algorithmic_flops"]
+           "config_seed", "workload_name", "pairs_reuse", "pairs_flattened", "algorithmic_flops",
+           "make_chain_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -204,6 +205,28 @@ def make_inputs(shape_or_cfg, seed: Optional[int] = None) -> Workload:
         do_r = _randn(gen, (T, Hq, D), 1.0, dt)
     offsets = torch.tensor(shape.offsets, dtype=torch.int32)
     return Workload(shape, q_p, k_p, v_p, q_r, k_r, v_r, do_p, do_r, offsets)
+
+
+def make_chain_inputs(P: int, lens: Sequence[int], W: int, Hq: int, Hkv: int, D: int, layers: int,
+                      seed: int, dtype: torch.dtype = torch.float64):
+    """Inputs of an L-layer attention chain over a replay tree, drawn in this order from one
+    CPU generator: prompt states x_p [P][W], packed branch states x_r [T_R][W], then per layer
+    wq [W][Hq*D], wk [W][Hkv*D], wv [W][Hkv*D] (N(0, 1/W)) and wo [Hq*D][W] (N(0, 1/(Hq*D))),
+    then the upstream gradients g_p [P][W] and g_r [T_R][W] (N(0, 1)). Returns
+    (x_p, x_r, offsets list, [(wq, wk, wv, wo), ...], g_p, g_r)."""
+    g = torch.Generator().manual_seed(int(seed))
+    T = int(sum(lens))
+    off = [0]
+    for r in lens:
+        off.append(off[-1] + int(r))
+
+    def rn(*shape, std=1.0):
+        return (torch.randn(*shape, generator=g, dtype=torch.float64) * std).to(dtype)
+    x_p = rn(P, W)
+    x_r = rn(T, W)
+    ws = [(rn(W, Hq * D, std=W ** -0.5), rn(W, Hkv * D, std=W ** -0.5), rn(W, Hkv * D, std=W ** -0.5),
+           rn(Hq * D, W, std=(Hq * D) ** -0.5)) for _ in range(layers)]
+    return x_p, x_r, off, ws, rn(P, W), rn(T, W)
 
 
 # ---- work accounting (counts of (query, key) pairs; no attention arithmetic) ----
