@@ -27,7 +27,9 @@
  * rounded once, to nearest even. Every device pointer must be 16-byte aligned.
  *
  * Ownership: the caller allocates every buffer, the workspace included (size from
- * augtree_workspace_bytes). The library allocates, frees and synchronises nothing, keeps
+ * augtree_workspace_bytes). The library allocates no device memory (only the host-side
+ * planner call augtree_assign_units uses host scratch of its own), frees and synchronises
+ * nothing, keeps
  * no pointer after a call returns, and enqueues all work on `stream` (a hipStream_t; NULL
  * is the null stream). Buffers must stay alive until that work completes.
  *
@@ -56,7 +58,7 @@
 extern "C" {
 #endif
 
-#define AUGTREE_ABI_VERSION 2
+#define AUGTREE_ABI_VERSION 3
 #define AUGTREE_MAX_BRANCHES 128
 
 typedef enum { AUGTREE_F32 = 0, AUGTREE_BF16 = 1 } augtree_dtype;
@@ -229,6 +231,26 @@ augtree_status augtree_prefill_dq(const augtree_dims *dims, const void *q_p, con
                                   const void *v_p, const float *lse_p, const float *rowdot_p,
                                   const void *do_p, void *dq_p, void *ws, size_t ws_bytes,
                                   void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Replay-unit assignment of the online planner (§3.4, "Replay units and grid assignment"):
+ * place num_units replay units (one complete response path each) with work estimates w on a
+ * grid of `rounds` response-replay rounds x `lanes` replay lanes per round, every cell holding
+ * at least one unit, minimising  sum over rounds of (largest lane load in the round).
+ * Exact (dynamic programming over subsets of units) when num_units <= exact_max, otherwise
+ * largest-first greedy: units by decreasing weight (equal weights: lower index first), each to
+ * the cell whose use raises the objective least, empty cells first while any remain (equal
+ * rises: the less loaded cell, then the lower cell index).
+ * in:  w HOST [num_units], finite and >= 0; rounds, lanes >= 1; rounds * lanes <= num_units;
+ *      0 <= exact_max <= AUGTREE_ASSIGN_EXACT_MAX (the exact path takes about
+ *      (rounds + lanes) * 3^num_units / 2 steps and 12 * lanes * 2^num_units bytes of host
+ *      memory).
+ * out: cell HOST [num_units]: round * lanes + lane of each unit; *cost: the objective.
+ * Host only: touches no device memory or stream. Deterministic for identical inputs. */
+#define AUGTREE_ASSIGN_EXACT_MAX 16
+augtree_status augtree_assign_units(const double *w, int32_t num_units, int32_t rounds,
+                                    int32_t lanes, int32_t exact_max, int32_t *cell,
+                                    double *cost);
 
 /* Bytes of workspace operation `op` (AUGTREE_OP_*) needs for `dims`; 0 for invalid dims. */
 size_t augtree_workspace_bytes(const augtree_dims *dims, int op);

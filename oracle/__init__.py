@@ -12,3 +12,4 @@ tree mask, finite differences, and invariants of the mathematics).
 from .flat_attention import (rows_attention, flattened_tree_attention,  # noqa: F401
                              flattened_sampled_rows, branch_response_grads)
 from .flat_chain import flattened_chain  # noqa: F401
+from .assign import brute_force_assign, greedy_assign, grid_cost  # noqa: F401

@@ -32,13 +32,14 @@ AUGTREE_OP_PREFILL_KV_BWD = 9
 AUGTREE_OP_PREFILL_DQ = 10
 AUGTREE_MAX_BRANCHES = 128
 AUGTREE_MAX_PARTS = 8
+AUGTREE_ASSIGN_EXACT_MAX = 16
 
 ENTRY_POINTS = ["augtree_prefill_fwd", "augtree_replay_fwd", "augtree_replay_bwd",
                 "augtree_prefill_bwd", "augtree_replay_prompt_fwd", "augtree_replay_local_fwd",
                 "augtree_merge_partials", "augtree_row_dot", "augtree_replay_prompt_bwd",
                 "augtree_replay_local_bwd", "augtree_replay_dq", "augtree_prefill_kv_bwd",
-                "augtree_prefill_dq", "augtree_workspace_bytes", "augtree_status_string",
-                "augtree_last_error", "augtree_abi_version"]
+                "augtree_prefill_dq", "augtree_assign_units", "augtree_workspace_bytes",
+                "augtree_status_string", "augtree_last_error", "augtree_abi_version"]
 
 
 class augtree_dims(ctypes.Structure):
@@ -85,7 +86,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.augtree_replay_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.augtree_prefill_kv_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.augtree_prefill_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for name in ENTRY_POINTS[:13]:
+    lib.augtree_assign_units.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+    for name in ENTRY_POINTS[:14]:
         getattr(lib, name).restype = st
     lib.augtree_workspace_bytes.argtypes = [P, ctypes.c_int]
     lib.augtree_workspace_bytes.restype = sz

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libaugtree.so")
-SOURCES = ["api.hip", "attn_fwd.hip", "attn_bwd.hip", "aux.hip"]
+SOURCES = ["api.hip", "attn_fwd.hip", "attn_bwd.hip", "aux.hip", "planner.hip"]
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          # packed fp32 VALU forms stay disabled: plain float code only

@@ -629,6 +629,12 @@ augtree_status check_key_range(const Shape& s, int kb, int ke) {
 }
 
 }  // namespace
+
+augtree_status set_error(augtree_status st, const char* msg) {
+  t_last_error = msg;
+  return st;
+}
+
 }  // namespace augtree
 
 using namespace augtree;

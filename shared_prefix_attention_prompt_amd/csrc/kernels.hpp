@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/augtree.h"
 #include "common.hpp"
 
 namespace augtree {
@@ -136,6 +137,9 @@ struct SplitReduceArgs {   // out[i] = sum_s part[s][i], s = 0..nsplit-1 in orde
 // many query heads of one kv group) and query rows per forward workgroup.
 int heads_per_wg(int group);
 int fwd_rows_per_wg(int group);
+
+// Records `msg` as the calling thread's last error (augtree_last_error) and returns st.
+augtree_status set_error(augtree_status st, const char* msg);
 
 hipError_t launch_transpose(int dtype, int D, const TransposeArgs& a, hipStream_t s);
 hipError_t launch_statpack(const StatPackArgs& a, hipStream_t s);

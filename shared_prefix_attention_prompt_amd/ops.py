@@ -6,6 +6,7 @@ float32 or bfloat16, with the layouts of include/augtree.h.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 from typing import Optional, Sequence, Tuple
 
@@ -303,3 +304,15 @@ def prefill_dq(tr: Tree, q_p, k_p, v_p, lse_p, rowdot_p, do_p, out=None, ws=None
                                  rowdot_p.data_ptr(), do_p.data_ptr(), dq.data_ptr(), wp, wn, tr.stream())
     _lib._check(st, "augtree_prefill_dq")
     return dq
+
+
+def assign_units(weights: Sequence[float], rounds: int, lanes: int, exact_max: int = 12):
+    """Replay-unit assignment (augtree_assign_units): (cell of each unit, objective), where cell
+    = round * lanes + lane and the objective is the sum over rounds of the largest lane load."""
+    n = len(weights)
+    w = (ctypes.c_double * max(n, 1))(*[float(x) for x in weights])
+    cells = (ctypes.c_int32 * max(n, 1))()
+    cost = ctypes.c_double(0.0)
+    _lib._check(_lib.load().augtree_assign_units(w, int(n), int(rounds), int(lanes), int(exact_max), cells,
+                                                 ctypes.byref(cost)), "augtree_assign_units")
+    return [int(cells[k]) for k in range(n)], float(cost.value)

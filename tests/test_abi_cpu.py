@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert _lib.abi_version() == 2
+    assert _lib.abi_version() == 3
     assert _lib.status_string(_lib.AUGTREE_OK) == "AUGTREE_OK"
     assert _lib.status_string(_lib.AUGTREE_ERR_WORKSPACE) == "AUGTREE_ERR_WORKSPACE"
     assert _lib.status_string(99) == "AUGTREE_ERR_UNKNOWN"
