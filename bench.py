@@ -55,13 +55,14 @@ def stage_flops(shape):
     }
 
 
-def stage_bytes(shape):
-    """Algorithmic HBM bytes of the HBM-bound stages (per launch)."""
+def stage_bytes(shape, parts: int = 2):
+    """Algorithmic HBM bytes of the HBM-bound stages (per launch); ``parts`` partial states
+    per branch row are merged (2: the whole prompt and the branch)."""
     T, P, D, Hq = shape.T, shape.P, shape.D, shape.Hq
     esz = 2 if shape.dtype == "bf16" else 4
     return {
-        # two fp32 partial outputs + two LSEs read, output + LSE written
-        "merge": T * Hq * (2 * 4 * D + 2 * 4 + esz * D + 4),
+        # the fp32 partial outputs and LSEs read, output + LSE written
+        "merge": T * Hq * (parts * (4 * D + 4) + esz * D + 4),
         # O and dO read, one float written
         "row_dot_r": T * Hq * (2 * esz * D + 4),
         "row_dot_p": P * Hq * (2 * esz * D + 4),
@@ -197,6 +198,10 @@ def main() -> int:
                          "0 (default): three when the kernels' grids are too small to fill the GPU")
     ap.add_argument("--no-gemm-reference", action="store_true",
                     help="skip timing the vendor bf16 GEMM reported beside the roofline peak")
+    ap.add_argument("--kv-shards", type=int, default=1, choices=range(1, 8), metavar="{1..7}",
+                    help="split the prompt K/V into this many stationary shards (the paper's MoveQ "
+                         "layout): the replay forward and the prompt K/V gradient run once per "
+                         "shard's key range and the merge combines shards + 1 partial states")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run a plain elementwise copy of this many MiB "
                          "three times (a known-size kernel to scale HBM byte counters by)")
@@ -241,6 +246,13 @@ def main() -> int:
         "dq_r": torch.empty_like(t["q_r"]), "dk_p": torch.empty_like(t["k_p"]),
         "dv_p": torch.empty_like(t["v_p"]), "dq_p": torch.empty_like(t["q_p"]),
     }
+    nsh = args.kv_shards
+    cuts = [min(s.P, round(s.P * i / nsh / 256) * 256) for i in range(nsh)] + [s.P]
+    if any(b <= a for a, b in zip(cuts, cuts[1:])):
+        print(f"--kv-shards {nsh}: the prompt of {s.P} keys cannot be cut into {nsh} non-empty "
+              "ranges of whole 256-key blocks", file=sys.stderr)
+        return 2
+    shard_bufs = [(tr.empty(s.T, s.Hq, s.D, dtype=f32), tr.empty(s.Hq, s.T, dtype=f32)) for _ in range(nsh - 1)]
     nws = max(_lib.workspace_bytes(tr.dims, op) for op in range(11))
     main = torch.cuda.current_stream(dev)
     nstreams = args.streams if args.streams > 0 else (3 if small_grid(s) else 1)
@@ -251,16 +263,17 @@ def main() -> int:
         "prefill_fwd": lambda ws: _lib._check(_lib.augtree_prefill_fwd(
             tr.dims, t["q_p"].data_ptr(), t["k_p"].data_ptr(), t["v_p"].data_ptr(), b["o_p"].data_ptr(),
             b["lse_p"].data_ptr(), ws.data_ptr(), ws.numel(), tr.stream()), "augtree_prefill_fwd"),
-        "replay_prompt_fwd": lambda ws: ops.replay_prompt_fwd(tr, t["k_p"], t["v_p"], t["q_r"],
-                                                              out=(b["oa"], b["la"]), ws=ws),
+        "replay_prompt_fwd": lambda ws: [ops.replay_prompt_fwd(
+            tr, t["k_p"], t["v_p"], t["q_r"], cuts[i], cuts[i + 1],
+            out=(b["oa"], b["la"]) if i == 0 else shard_bufs[i - 1], ws=ws) for i in range(nsh)],
         "replay_local_fwd": lambda ws: ops.replay_local_fwd(tr, t["q_r"], t["k_r"], t["v_r"],
                                                             out=(b["ob"], b["lb"]), ws=ws),
-        "merge": lambda ws: ops.merge_partials(tr, [(b["oa"], b["la"]), (b["ob"], b["lb"])],
+        "merge": lambda ws: ops.merge_partials(tr, [(b["oa"], b["la"])] + shard_bufs + [(b["ob"], b["lb"])],
                                                out=(b["o_r"], b["lse_r"])),
         "row_dot_r": lambda ws: ops.row_dot(tr, b["o_r"], t["do_r"], out=b["rd_r"]),
-        "replay_prompt_bwd": lambda ws: ops.replay_prompt_bwd(
-            tr, t["k_p"], t["v_p"], t["q_r"], b["lse_r"], b["rd_r"], t["do_r"], dk_acc=b["dk_acc"],
-            dv_acc=b["dv_acc"], ws=ws),
+        "replay_prompt_bwd": lambda ws: [ops.replay_prompt_bwd(
+            tr, t["k_p"], t["v_p"], t["q_r"], b["lse_r"], b["rd_r"], t["do_r"], cuts[i], cuts[i + 1],
+            dk_acc=b["dk_acc"], dv_acc=b["dv_acc"], ws=ws) for i in range(nsh)],
         "replay_local_bwd": lambda ws: ops.replay_local_bwd(
             tr, t["q_r"], t["k_r"], t["v_r"], b["lse_r"], b["rd_r"], t["do_r"], out=(b["dk_r"], b["dv_r"]), ws=ws),
         "replay_dq": lambda ws: ops.replay_dq(tr, t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], b["lse_r"],
@@ -329,7 +342,7 @@ def main() -> int:
     tflops = flops / (ms_per_step / 1e3) / 1e12
     peak = BF16_PEAK_TFLOPS if s.dtype == "bf16" else F32_PEAK_TFLOPS
     sf = {k: v for k, v in stage_flops(s).items() if k in stages}
-    sb = {k: v for k, v in stage_bytes(s).items() if k in stages}
+    sb = {k: v for k, v in stage_bytes(s, parts=nsh + 1).items() if k in stages}
     kernels = {}
     for name in stages:
         ms = stage_ms[name]
@@ -341,7 +354,7 @@ def main() -> int:
         kernels[name] = entry
     dom = max(sf, key=lambda n: stage_ms[n])
     achieved = sf[dom] / (stage_ms[dom] / 1e3) / 1e12
-    tr_rec = stored_traffic(dom) if cfg == 4 else None
+    tr_rec = stored_traffic(dom) if cfg == 4 and nsh == 1 else None
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": tr_rec["bytes_per_launch"] if tr_rec else None,
@@ -372,7 +385,8 @@ def main() -> int:
         "config": {"workload": workload_name(cfg), "P": s.P, "G": s.G, "branch_lens": list(s.lens),
                    "T_R": s.T, "Hq": s.Hq, "Hkv": s.Hkv, "D": s.D,
                    "passes": "fwd+bwd" if s.backward else "fwd",
-                   "alg_flops": flops, "seed": config_seed(cfg), "streams": nstreams},
+                   "alg_flops": flops, "seed": config_seed(cfg), "streams": nstreams,
+                   "kv_shards": nsh},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
         "wall_s": round(wall, 3),
     }
