@@ -246,6 +246,9 @@ augtree_status augtree_prefill_dq(const augtree_dims *dims, const void *q_p, con
  *      (rounds + lanes) * 3^num_units / 2 steps and 12 * lanes * 2^num_units bytes of host
  *      memory).
  * out: cell HOST [num_units]: round * lanes + lane of each unit; *cost: the objective.
+ * Errors: AUGTREE_ERR_INVALID_ARGUMENT for a NULL pointer, a size out of range, fewer units
+ * than cells, a negative or non-finite weight, or host memory running out on the exact path;
+ * nothing is written then.
  * Host only: touches no device memory or stream. Deterministic for identical inputs. */
 #define AUGTREE_ASSIGN_EXACT_MAX 16
 augtree_status augtree_assign_units(const double *w, int32_t num_units, int32_t rounds,

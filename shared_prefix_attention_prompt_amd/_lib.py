@@ -131,6 +131,12 @@ def _check(status: int, where: str) -> None:
         raise AugtreeError(status, where, last_error())
 
 
+def augtree_assign_units(w, num_units, rounds, lanes, exact_max, cell, cost) -> int:
+    """w: host double[num_units]; cell: host int32[num_units]; cost: host double (ctypes
+    arrays or byref pointers)."""
+    return load().augtree_assign_units(w, num_units, rounds, lanes, exact_max, cell, cost)
+
+
 def augtree_prefill_fwd(dims, q_p, k_p, v_p, o_p, lse_p, ws, ws_bytes, stream) -> int:
     return load().augtree_prefill_fwd(ctypes.byref(dims), q_p, k_p, v_p, o_p, lse_p, ws, ws_bytes, stream)
 

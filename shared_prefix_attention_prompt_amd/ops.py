@@ -313,6 +313,6 @@ def assign_units(weights: Sequence[float], rounds: int, lanes: int, exact_max: i
     w = (ctypes.c_double * max(n, 1))(*[float(x) for x in weights])
     cells = (ctypes.c_int32 * max(n, 1))()
     cost = ctypes.c_double(0.0)
-    _lib._check(_lib.load().augtree_assign_units(w, int(n), int(rounds), int(lanes), int(exact_max), cells,
-                                                 ctypes.byref(cost)), "augtree_assign_units")
+    _lib._check(_lib.augtree_assign_units(w, int(n), int(rounds), int(lanes), int(exact_max), cells,
+                                          ctypes.byref(cost)), "augtree_assign_units")
     return [int(cells[k]) for k in range(n)], float(cost.value)
