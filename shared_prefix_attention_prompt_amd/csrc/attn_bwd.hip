@@ -421,10 +421,29 @@ __global__ __launch_bounds__(512, 2) void dq_kernel(DqArgs a) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       f32x16 sacc = zero16(), pacc = zero16();
+      if constexpr (M::E == 8) {
+        // K and V fragments read two matrix ops ahead through a ring of three (scheduling
+        // barriers keep the order)
+        constexpr int NI = 2 * KS;
+        auto fkv = [&](int i) {
+          return tile_frag<T, RBN>((i & 1) ? v_ : k_, kb * 32 + c, (i >> 1) * M::K + g * M::E);
+        };
+        typename M::frag fr[3];
+        fr[0] = fkv(0);
+        fr[1] = fkv(1);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        sacc = M::run(tile_frag<T, RBN>(k_, kb * 32 + c, s * M::K + g * M::E), qf[s], sacc);
-        pacc = M::run(tile_frag<T, RBN>(v_, kb * 32 + c, s * M::K + g * M::E), of[s], pacc);
+        for (int i = 0; i < NI; ++i) {
+          if (i + 2 < NI) fr[(i + 2) % 3] = fkv(i + 2);
+          if (i & 1) pacc = M::run(fr[i % 3], of[i >> 1], pacc);
+          else sacc = M::run(fr[i % 3], qf[i >> 1], sacc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          sacc = M::run(tile_frag<T, RBN>(k_, kb * 32 + c, s * M::K + g * M::E), qf[s], sacc);
+          pacc = M::run(tile_frag<T, RBN>(v_, kb * 32 + c, s * M::K + g * M::E), of[s], pacc);
+        }
       }
       // the mask test is taken once per tile, not per element, so that the unmasked
       // element loop is one straight block
@@ -441,12 +460,30 @@ __global__ __launch_bounds__(512, 2) void dq_kernel(DqArgs a) {
       };
       if (need_mask) softmax_grad(std::true_type{});
       else softmax_grad(std::false_type{});
+      if constexpr (M::E == 8) {
+        // K^T fragments read two matrix ops ahead through a ring of three
+        constexpr int NQ = NS * DB;
+        const typename M::frag df0 = acc_frag<T>(pacc, 0);
+        const typename M::frag df1 = acc_frag<T>(pacc, 1);
+        auto fk = [&](int i) { return tile_frag<T, RBT>(kt_, (i % DB) * 32 + c, kb * 32 + tread<T>(i / DB, g)); };
+        typename M::frag fr[3];
+        fr[0] = fk(0);
+        fr[1] = fk(1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const typename M::frag df = acc_frag<T>(pacc, s);
+        for (int i = 0; i < NQ; ++i) {
+          if (i + 2 < NQ) fr[(i + 2) % 3] = fk(i + 2);
+          dqt[i % DB] = M::run(fr[i % 3], i < DB ? df0 : df1, dqt[i % DB]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          dqt[db] = M::run(tile_frag<T, RBT>(kt_, db * 32 + c, kb * 32 + tread<T>(s, g)), df, dqt[db]);
+        for (int s = 0; s < NS; ++s) {
+          const typename M::frag df = acc_frag<T>(pacc, s);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            dqt[db] = M::run(tile_frag<T, RBT>(kt_, db * 32 + c, kb * 32 + tread<T>(s, g)), df, dqt[db]);
+        }
       }
     }
   };
