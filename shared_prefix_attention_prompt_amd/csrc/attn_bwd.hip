@@ -218,11 +218,29 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
     const int row0 = stage_row0[decltype(S)::value];
     if (causal && row0 + 31 < wk_lo) return;  // every query of the tile precedes every key
     f32x16 sacc = zero16(), pacc = zero16();
+    if constexpr (M::E == 8) {
+      // Q, dO and V fragments read one step (two matrix ops) ahead
+      auto fq = [&](int s) { return tile_frag<T, RBN>(q_, c, s * M::K + g * M::E); };
+      auto fo = [&](int s) { return tile_frag<T, RBN>(o_, c, s * M::K + g * M::E); };
+      auto fv = [&](int s) { return tile_frag<T, RBN>(lv, w * 32 + c, s * M::K + g * M::E); };
+      typename M::frag q0 = fq(0), o0 = fo(0), v0 = fv(0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      sacc = M::run(tile_frag<T, RBN>(q_, c, s * M::K + g * M::E), kf[s], sacc);
-      pacc = M::run(tile_frag<T, RBN>(o_, c, s * M::K + g * M::E),
-                    tile_frag<T, RBN>(lv, w * 32 + c, s * M::K + g * M::E), pacc);
+      for (int s = 0; s < KS; ++s) {
+        typename M::frag q1 = q0, o1 = o0, v1 = v0;
+        if (s + 1 < KS) { q1 = fq(s + 1); o1 = fo(s + 1); v1 = fv(s + 1); }
+        sacc = M::run(q0, kf[s], sacc);
+        pacc = M::run(o0, v0, pacc);
+        __builtin_amdgcn_sched_barrier(0);
+        q0 = q1; o0 = o1; v0 = v1;
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        sacc = M::run(tile_frag<T, RBN>(q_, c, s * M::K + g * M::E), kf[s], sacc);
+        pacc = M::run(tile_frag<T, RBN>(o_, c, s * M::K + g * M::E),
+                      tile_frag<T, RBN>(lv, w * 32 + c, s * M::K + g * M::E), pacc);
+      }
     }
     auto softmax_grad = [&](auto masked) {
 #pragma unroll
@@ -244,14 +262,36 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
     };
     if (causal && row0 < wk_lo + 31) softmax_grad(std::true_type{});  // the diagonal tile
     else softmax_grad(std::false_type{});
+    if constexpr (M::E == 8) {
+      // dO^T and Q^T fragments read two matrix ops ahead through a ring of three
+      constexpr int NP = NS * DB * 2;
+      const typename M::frag pf0 = acc_frag<T>(sacc, 0), pf1 = acc_frag<T>(sacc, 1);
+      const typename M::frag df0 = acc_frag<T>(pacc, 0), df1 = acc_frag<T>(pacc, 1);
+      auto ft = [&](int i) {
+        return tile_frag<T, RBT>((i & 1) ? qt_ : ot_, ((i >> 1) % DB) * 32 + c, tread<T>((i >> 1) / DB, g));
+      };
+      typename M::frag fr[3];
+      fr[0] = ft(0);
+      fr[1] = ft(1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const typename M::frag pf = acc_frag<T>(sacc, s);
-      const typename M::frag df = acc_frag<T>(pacc, s);
+      for (int i = 0; i < NP; ++i) {
+        if (i + 2 < NP) fr[(i + 2) % 3] = ft(i + 2);
+        const int db = (i >> 1) % DB, s = (i >> 1) / DB;
+        if (i & 1) dkt[db] = M::run(fr[i % 3], s == 0 ? df0 : df1, dkt[db]);
+        else dvt[db] = M::run(fr[i % 3], s == 0 ? pf0 : pf1, dvt[db]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dvt[db] = M::run(tile_frag<T, RBT>(ot_, db * 32 + c, tread<T>(s, g)), pf, dvt[db]);
-        dkt[db] = M::run(tile_frag<T, RBT>(qt_, db * 32 + c, tread<T>(s, g)), df, dkt[db]);
+      for (int s = 0; s < NS; ++s) {
+        const typename M::frag pf = acc_frag<T>(sacc, s);
+        const typename M::frag df = acc_frag<T>(pacc, s);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dvt[db] = M::run(tile_frag<T, RBT>(ot_, db * 32 + c, tread<T>(s, g)), pf, dvt[db]);
+          dkt[db] = M::run(tile_frag<T, RBT>(qt_, db * 32 + c, tread<T>(s, g)), df, dkt[db]);
+        }
       }
     }
   };
