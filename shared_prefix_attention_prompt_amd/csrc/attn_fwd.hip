@@ -209,16 +209,41 @@ __global__ __launch_bounds__(kFwdWaves * 64, 2) void attn_fwd_kernel(FwdArgs a) 
 #pragma unroll
           for (int r = 0; r < 16; ++r) pacc[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], sl2, -msc2));
       }
+      if constexpr (M::E == 8) {
+        // V^T fragments read two matrix ops ahead through a ring of three
+        constexpr int NP = KB * NS * DB;
+        auto fv = [&](int i) {
+          const int db = i % DB, ks = i / DB;  // ks = kb * NS + s
+          return tile_frag<T, RBV>(lv, db * 32 + c, (ks / NS) * 32 + tread<T>(ks % NS, g));
+        };
+        typename M::frag pfs[KB * NS];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const typename M::frag pf = acc_frag<T>(pacc[kb], s);
-          l_run = frag_sum(pf, l_run);
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            oacc[db] = M::run(tile_frag<T, RBV>(lv, db * 32 + c, kb * 32 + tread<T>(s, g)), pf, oacc[db]);
+        for (int ks = 0; ks < KB * NS; ++ks) {
+          pfs[ks] = acc_frag<T>(pacc[ks / NS], ks % NS);
+          l_run = frag_sum(pfs[ks], l_run);
         }
+        typename M::frag fr[3];
+        fr[0] = fv(0);
+        fr[1] = fv(1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          if (i + 2 < NP) fr[(i + 2) % 3] = fv(i + 2);
+          oacc[i % DB] = M::run(fr[i % 3], pfs[i / DB], oacc[i % DB]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const typename M::frag pf = acc_frag<T>(pacc[kb], s);
+            l_run = frag_sum(pf, l_run);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+              oacc[db] = M::run(tile_frag<T, RBV>(lv, db * 32 + c, kb * 32 + tread<T>(s, g)), pf, oacc[db]);
+          }
+      }
     }
   };
 
