@@ -136,10 +136,10 @@ def small_grid(shape):
 
 def schedule(stages, nstreams):
     """Issue plan: (kind, stream, name) with kind "run", "mark" (record an event) or "wait".
-    Three streams: the prompt prefill (and its row dot) beside the replay; the branch-local
-    forward beside the replay against the prompt; after the merge, the prompt K/V gradient
-    beside the branch K/V gradient and branch dQ; the prefill backward steps last on the two
-    busy streams. Every dependency of the path is an event; results are identical to the
+    Three streams: the prompt prefill, its row dot and the prefill dQ on one stream, beside the
+    replay; the branch-local forward beside the replay against the prompt; after the merge, the
+    prompt K/V gradient (then the prefill K/V gradient, which adds it) beside the branch K/V
+    gradient and branch dQ. Every dependency of the path is an event; results are identical to the
     one-stream order (no step's arithmetic depends on the schedule)."""
     if nstreams == 1:
         return [("run", 0, n) for n in stages]
@@ -151,7 +151,7 @@ def schedule(stages, nstreams):
           ("run", 1, "row_dot_r"), ("mark", 1, "rdr"), ("run", 1, "replay_prompt_bwd"),
           ("wait", 2, "rdr"), ("run", 2, "replay_local_bwd"), ("run", 2, "replay_dq"),
           ("wait", 1, "rdp"), ("run", 1, "prefill_kv_bwd"),
-          ("wait", 2, "rdp"), ("run", 2, "prefill_dq")]
+          ("run", 0, "prefill_dq")]
     return p
 
 
