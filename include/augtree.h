@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define AUGTREE_ABI_VERSION 3
+#define AUGTREE_ABI_VERSION 4
 #define AUGTREE_MAX_BRANCHES 128
 
 typedef enum { AUGTREE_F32 = 0, AUGTREE_BF16 = 1 } augtree_dtype;
@@ -163,7 +163,8 @@ augtree_status augtree_prefill_bwd(const augtree_dims *dims, const void *q_p, co
 
 /* Partial state of every branch row over prompt keys [key_begin, key_end), no mask
  * (§3.3 MoveQ: a stationary prompt K/V shard evaluates all branch queries).
- * 0 <= key_begin < key_end <= P. Workspace: AUGTREE_OP_REPLAY_PROMPT_FWD. */
+ * 0 <= key_begin < key_end <= P. Workspace: augtree_range_workspace_bytes(dims,
+ * AUGTREE_OP_REPLAY_PROMPT_FWD, key_begin, key_end) (a transposed copy of the range's V). */
 augtree_status augtree_replay_prompt_fwd(const augtree_dims *dims, const void *k_p,
                                          const void *v_p, const void *q_r, int32_t key_begin,
                                          int32_t key_end, float *o_part, float *lse_part,
@@ -194,7 +195,9 @@ augtree_status augtree_row_dot(const augtree_dims *dims, int32_t rows, const voi
 /* Prompt K/V gradient from every branch row, for prompt keys [key_begin, key_end): writes
  * rows [key_begin, key_end) of dk_p_acc/dv_p_acc [P][Hkv][D] float32 with the sum over all
  * branches and over the query heads of each group (§3.2, equation after Eq. 1), in a fixed
- * order. Workspace: augtree_workspace_bytes(dims, AUGTREE_OP_REPLAY_PROMPT_BWD). */
+ * order. Workspace: augtree_range_workspace_bytes(dims, AUGTREE_OP_REPLAY_PROMPT_BWD,
+ * key_begin, key_end): transposed Q/dO copies, row statistics and, when the range has few key
+ * tiles, split partial sums (their count depends on dims and range only). */
 augtree_status augtree_replay_prompt_bwd(const augtree_dims *dims, const void *k_p,
                                          const void *v_p, const void *q_r, const float *lse_r,
                                          const float *rowdot_r, const void *do_r,
@@ -255,8 +258,17 @@ augtree_status augtree_assign_units(const double *w, int32_t num_units, int32_t 
                                     int32_t lanes, int32_t exact_max, int32_t *cell,
                                     double *cost);
 
-/* Bytes of workspace operation `op` (AUGTREE_OP_*) needs for `dims`; 0 for invalid dims. */
+/* Bytes of workspace operation `op` (AUGTREE_OP_*) needs for `dims`; 0 for invalid dims.
+ * For the ops that take a prompt key range this covers every range. */
 size_t augtree_workspace_bytes(const augtree_dims *dims, int op);
+
+/* Bytes of workspace one call of `op` over prompt keys [key_begin, key_end) needs: a
+ * stationary prompt-K/V shard of §3.3 (MoveQ) sizes its own workspace with this. Never more
+ * than augtree_workspace_bytes(dims, op). For ops without a key range it equals
+ * augtree_workspace_bytes. 0 for invalid dims or an empty or out-of-range key range.
+ * Host only. */
+size_t augtree_range_workspace_bytes(const augtree_dims *dims, int op, int32_t key_begin,
+                                     int32_t key_end);
 
 /* Static text of a status code. */
 const char *augtree_status_string(augtree_status status);

@@ -39,6 +39,7 @@ ENTRY_POINTS = ["augtree_prefill_fwd", "augtree_replay_fwd", "augtree_replay_bwd
                 "augtree_merge_partials", "augtree_row_dot", "augtree_replay_prompt_bwd",
                 "augtree_replay_local_bwd", "augtree_replay_dq", "augtree_prefill_kv_bwd",
                 "augtree_prefill_dq", "augtree_assign_units", "augtree_workspace_bytes",
+                "augtree_range_workspace_bytes",
                 "augtree_status_string", "augtree_last_error", "augtree_abi_version"]
 
 
@@ -91,6 +92,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, name).restype = st
     lib.augtree_workspace_bytes.argtypes = [P, ctypes.c_int]
     lib.augtree_workspace_bytes.restype = sz
+    lib.augtree_range_workspace_bytes.argtypes = [P, ctypes.c_int, i32, i32]
+    lib.augtree_range_workspace_bytes.restype = sz
     lib.augtree_status_string.argtypes = [ctypes.c_int]
     lib.augtree_status_string.restype = ctypes.c_char_p
     lib.augtree_last_error.argtypes = []
@@ -124,6 +127,11 @@ def abi_version() -> int:
 
 def workspace_bytes(dims: augtree_dims, op: int) -> int:
     return int(load().augtree_workspace_bytes(ctypes.byref(dims), int(op)))
+
+
+def range_workspace_bytes(dims: augtree_dims, op: int, key_begin: int, key_end: int) -> int:
+    return int(load().augtree_range_workspace_bytes(ctypes.byref(dims), int(op), int(key_begin),
+                                                    int(key_end)))
 
 
 def _check(status: int, where: str) -> None:

@@ -220,23 +220,40 @@ size_t prefill_split_ws(const Shape& s) {
   return ps.nz > 1 ? align_up((size_t)2 * ps.nz * s.P * s.Hkv * s.D * sizeof(float)) : 0;
 }
 
-// Float count of the split partials for a key range (split * keys * Hkv * D per tensor).
-size_t prompt_split_floats(const Shape& s, int nkeys) {
-  const int n = prompt_split(s, nkeys);
-  return n > 1 ? (size_t)n * nkeys * s.Hkv * s.D : 0;
-}
-
-// Split partials of augtree_replay_prompt_bwd: sized for the largest key range a call may use
-// (the maximum over whole-tile ranges, which bounds every range).
-size_t prompt_split_ws(const Shape& s) {
-  size_t best = 0;
+// Key rows of split partials (parts x keys) reserved for augtree_replay_prompt_bwd: the
+// largest parts x keys over ranges of whole 256-key blocks (the whole prompt included). A
+// range of any other length takes at most this many (split_for_range clamps its part count),
+// so the reserve depends on the dims alone.
+int64_t prompt_split_cap(const Shape& s) {
+  int64_t best = 0;
   const int nkt = (s.P + kDkdvKeysPerWG - 1) / kDkdvKeysPerWG;
   for (int t = 1; t <= nkt; ++t) {
     const int nk = t == nkt ? s.P : t * kDkdvKeysPerWG;
-    const size_t f = prompt_split_floats(s, nk);
-    if (f > best) best = f;
+    const int n = prompt_split(s, nk);
+    if (n > 1) best = std::max<int64_t>(best, (int64_t)n * nk);
   }
-  return align_up(2 * best * sizeof(float));
+  return best;
+}
+
+// Split count of the prompt dK/dV pass over `nkeys` keys: the modelled best, lowered where
+// n x nkeys would exceed the reserve (a choice of summation grouping only: any count gives the
+// same sums up to fp32 rounding, and it depends on dims and range alone, so results stay
+// bitwise reproducible).
+int split_for_range(const Shape& s, int nkeys, int64_t cap_keys) {
+  int n = prompt_split(s, nkeys);
+  if (n > 1 && (int64_t)n * nkeys > cap_keys) n = (int)(cap_keys / nkeys);
+  return n > 1 ? n : 1;
+}
+
+// Bytes of split partials (dK and dV) for a reserve of cap_keys key rows.
+size_t split_bytes(const Shape& s, int64_t cap_keys) {
+  return align_up((size_t)2 * cap_keys * s.Hkv * s.D * sizeof(float));
+}
+
+// Reserve of the composite backward, which only runs the range [0, P).
+int64_t prompt_split_cap_whole(const Shape& s) {
+  const int n = prompt_split(s, s.P);
+  return n > 1 ? (int64_t)n * s.P : 0;
 }
 
 // Layout of a workspace as consecutive 256-byte aligned pieces.
@@ -273,7 +290,7 @@ ReplayBwdWs replay_bwd_ws(const Shape& s) {
   w.stats = l.add(st_resp(s));
   w.kpt = l.add(tr_prompt(s, s.Hkv));
   w.krt = l.add(tr_resp(s, s.Hkv));
-  w.split = l.add(prompt_split_ws(s));
+  w.split = l.add(split_bytes(s, prompt_split_cap_whole(s)));
   w.total = l.total;
   return w;
 }
@@ -298,7 +315,7 @@ size_t op_workspace(const Shape& s, int op) {
     case AUGTREE_OP_REPLAY_FWD: return replay_fwd_ws(s).total;
     case AUGTREE_OP_REPLAY_BWD: return replay_bwd_ws(s).total;
     case AUGTREE_OP_PREFILL_BWD: return prefill_bwd_ws(s).total;
-    case AUGTREE_OP_REPLAY_PROMPT_BWD: return 2 * tr_resp(s, s.Hq) + st_resp(s) + prompt_split_ws(s);
+    case AUGTREE_OP_REPLAY_PROMPT_BWD: return 2 * tr_resp(s, s.Hq) + st_resp(s) + split_bytes(s, prompt_split_cap(s));
     case AUGTREE_OP_REPLAY_PROMPT_FWD: return tr_prompt(s, s.Hkv);
     case AUGTREE_OP_REPLAY_LOCAL_FWD: return tr_resp(s, s.Hkv);
     case AUGTREE_OP_REPLAY_LOCAL_BWD: return 2 * tr_resp(s, s.Hq) + st_resp(s);
@@ -307,6 +324,19 @@ size_t op_workspace(const Shape& s, int op) {
     case AUGTREE_OP_PREFILL_DQ: return tr_prompt(s, s.Hkv);
   }
   return 0;
+}
+
+// Workspace of a call over prompt keys [kb, ke) (ops that take a key range; others: op_workspace).
+size_t range_workspace(const Shape& s, int op, int kb, int ke) {
+  const int nkeys = ke - kb;
+  switch (op) {
+    case AUGTREE_OP_REPLAY_PROMPT_FWD: return tr_bytes(s, s.Hkv, pad64(nkeys));
+    case AUGTREE_OP_REPLAY_PROMPT_BWD: {
+      const int n = split_for_range(s, nkeys, prompt_split_cap(s));
+      return 2 * tr_resp(s, s.Hq) + st_resp(s) + (n > 1 ? split_bytes(s, (int64_t)n * nkeys) : 0);
+    }
+  }
+  return op_workspace(s, op);
 }
 
 augtree_status check_ws(const void* ws, size_t have, size_t need) {
@@ -486,11 +516,17 @@ augtree_status step_row_dot(const Shape& s, int rows, const void* o, const void*
 }
 
 // qrt/dort: transposed branch copies of q_r / do_r; split: split-partial workspace
+// split: split-partial region of split_have bytes; cap_keys: the reserve the split count is
+// clamped to (parts x keys)
 augtree_status step_replay_prompt_bwd(const Shape& s, const void* k_p, const void* v_p, const void* q_r,
                                       const void* qrt, const float* stats, const void* do_r, const void* dort,
-                                      int kb, int ke, float* dk_acc, float* dv_acc, void* split, hipStream_t st) {
+                                      int kb, int ke, float* dk_acc, float* dv_acc, void* split, size_t split_have,
+                                      int64_t cap_keys, hipStream_t st) {
   const int nkeys = ke - kb;
-  const int nsplit = prompt_split(s, nkeys);
+  const int nsplit = split_for_range(s, nkeys, cap_keys);
+  if (nsplit > 1 && (size_t)2 * nsplit * nkeys * s.Hkv * s.D * sizeof(float) > split_have)
+    return fail(AUGTREE_ERR_WORKSPACE, "prompt dK/dV split partials of %d parts x %d keys exceed the %zu bytes "
+                "left in the workspace", nsplit, nkeys, split_have);
   const size_t koff = (size_t)kb * s.Hkv * s.D;
   const int64_t part = (int64_t)nkeys * s.Hkv * s.D;
   float* part_dk = static_cast<float*>(split);
@@ -659,6 +695,16 @@ const char* augtree_status_string(augtree_status st) {
 
 const char* augtree_last_error(void) { return t_last_error.c_str(); }
 
+size_t augtree_range_workspace_bytes(const augtree_dims* dims, int op, int32_t key_begin, int32_t key_end) {
+  Shape s;
+  const std::string saved = t_last_error;
+  if (check_dims(dims, &s) != AUGTREE_OK || key_begin < 0 || key_end > s.P || key_begin >= key_end) {
+    t_last_error = saved;
+    return 0;
+  }
+  return range_workspace(s, op, key_begin, key_end);
+}
+
 size_t augtree_workspace_bytes(const augtree_dims* dims, int op) {
   Shape s;
   const std::string saved = t_last_error;
@@ -678,7 +724,7 @@ augtree_status augtree_replay_prompt_fwd(const augtree_dims* dims, const void* k
   CHECK(check_dims(dims, &s));
   CHECK(check_key_range(s, key_begin, key_end));
   PTR(k_p); PTR(v_p); PTR(q_r); PTR(o_part); PTR(lse_part);
-  CHECK(check_ws(ws, ws_bytes, op_workspace(s, AUGTREE_OP_REPLAY_PROMPT_FWD)));
+  CHECK(check_ws(ws, ws_bytes, range_workspace(s, AUGTREE_OP_REPLAY_PROMPT_FWD, key_begin, key_end)));
   hipStream_t st = static_cast<hipStream_t>(stream);
   CHECK(transpose_range(s, v_p, s.Hkv, key_begin, key_end - key_begin, 64, ws, st));
   return step_replay_prompt_fwd(s, k_p, ws, q_r, key_begin, key_end, o_part, lse_part, st);
@@ -730,17 +776,18 @@ augtree_status augtree_replay_prompt_bwd(const augtree_dims* dims, const void* k
   CHECK(check_dims(dims, &s));
   CHECK(check_key_range(s, key_begin, key_end));
   PTR(k_p); PTR(v_p); PTR(q_r); PTR(lse_r); PTR(rowdot_r); PTR(do_r); PTR(dk_p_acc); PTR(dv_p_acc);
-  CHECK(check_ws(ws, ws_bytes, op_workspace(s, AUGTREE_OP_REPLAY_PROMPT_BWD)));
+  CHECK(check_ws(ws, ws_bytes, range_workspace(s, AUGTREE_OP_REPLAY_PROMPT_BWD, key_begin, key_end)));
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* qrt = ws;
   void* dort = at(ws, tr_resp(s, s.Hq));
   float* stats = reinterpret_cast<float*>(at(ws, 2 * tr_resp(s, s.Hq)));
   void* split = at(ws, 2 * tr_resp(s, s.Hq) + st_resp(s));
+  const size_t split_have = ws_bytes - (2 * tr_resp(s, s.Hq) + st_resp(s));
   CHECK(transpose_branches(s, q_r, s.Hq, 32, qrt, st));
   CHECK(transpose_branches(s, do_r, s.Hq, 32, dort, st));
   CHECK(pack_stats_branches(s, lse_r, rowdot_r, stats, st));
   return step_replay_prompt_bwd(s, k_p, v_p, q_r, qrt, stats, do_r, dort, key_begin, key_end, dk_p_acc, dv_p_acc,
-                                split, st);
+                                split, split_have, prompt_split_cap(s), st);
 }
 
 augtree_status augtree_replay_local_bwd(const augtree_dims* dims, const void* q_r, const void* k_r,
@@ -870,7 +917,7 @@ augtree_status augtree_replay_bwd(const augtree_dims* dims, const void* k_p, con
   CHECK(pack_stats_branches(s, lse_r, rowdot, stats, st));
   // prompt keys x all branches' rows (no mask): the branch sum of the prompt gradient
   CHECK(step_replay_prompt_bwd(s, k_p, v_p, q_r, at(ws, w.qrt), stats, do_r, at(ws, w.dort), 0, s.P, dk_p_acc,
-                               dv_p_acc, at(ws, w.split), st));
+                               dv_p_acc, at(ws, w.split), w.total - w.split, prompt_split_cap_whole(s), st));
   // branch keys x own-branch rows (causal)
   CHECK(step_replay_local_bwd(s, q_r, at(ws, w.qrt), k_r, v_r, stats, do_r, at(ws, w.dort), dk_r, dv_r, st));
   // dQ of every branch row: prompt keys, then own-branch keys

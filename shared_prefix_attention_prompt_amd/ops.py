@@ -31,6 +31,40 @@ def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _expect(name: str, t, shape, dtype) -> None:
+    """Raise ValueError unless t is a tensor of exactly this shape and dtype (checked before
+    anything reaches the library, so a mismatch never launches a kernel)."""
+    if not torch.is_tensor(t):
+        raise ValueError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _tree_sizes(q, k, offsets, q_name: str, k_name: str):
+    """(rows, Hq, Hkv, D, dtype) read from a query tensor [rows][Hq][D] and a key tensor
+    [rows'][Hkv][D], with the head and dtype rules of the interface checked."""
+    for name, t in ((q_name, q), (k_name, k)):
+        if not torch.is_tensor(t) or t.dim() != 3:
+            raise ValueError(f"{name} must be a 3-d tensor [rows][heads][head_dim]")
+    rows, Hq, D = (int(x) for x in q.shape)
+    Hkv = int(k.shape[1])
+    if q.dtype not in _DT:
+        raise ValueError(f"{q_name} has unsupported dtype {q.dtype} (float32 or bfloat16)")
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError(f"{q_name} has {Hq} heads, not a multiple of the {Hkv} heads of {k_name}")
+    if int(k.shape[2]) != D:
+        raise ValueError(f"{k_name} has head_dim {int(k.shape[2])}, {q_name} {D}")
+    return rows, Hq, Hkv, D, q.dtype
+
+
+def _check_offsets(off) -> int:
+    if len(off) < 2 or off[0] != 0 or any(b <= a for a, b in zip(off, off[1:])):
+        raise ValueError(f"offsets must start at 0 and increase strictly (every branch >= 1 row): {off[:8]}")
+    return off[-1]
+
+
 def _check_tensors(*named):
     dev = None
     for name, t in named:
@@ -65,9 +99,11 @@ def _workspace(dims, op, device):
 def prefill_fwd(q_p, k_p, v_p, scale: Optional[float] = None, offsets: Sequence[int] = (0, 1)
                 ) -> Tuple[torch.Tensor, torch.Tensor]:
     """Causal prompt attention: (o_p [P][Hq][D], lse_p [Hq][P] float32)."""
+    P, Hq, Hkv, D, dt = _tree_sizes(q_p, k_p, offsets, "q_p", "k_p")
+    _expect("k_p", k_p, (P, Hkv, D), dt)
+    _expect("v_p", v_p, (P, Hkv, D), dt)
     dev = _check_tensors(("q_p", q_p), ("k_p", k_p), ("v_p", v_p))
-    P, Hq, D = q_p.shape
-    dims, keep = _dims(P, _offsets_list(offsets), Hq, k_p.shape[1], D, scale, q_p.dtype)
+    dims, keep = _dims(P, _offsets_list(offsets), Hq, Hkv, D, scale, dt)
     o_p = torch.empty_like(q_p)
     lse_p = torch.empty(Hq, P, dtype=torch.float32, device=dev)
     ws, n = _workspace(dims, _lib.AUGTREE_OP_PREFILL_FWD, dev)
@@ -81,9 +117,17 @@ def replay_fwd(k_p, v_p, q_r, k_r, v_r, offsets, scale: Optional[float] = None
                ) -> Tuple[torch.Tensor, torch.Tensor]:
     """Branch rows against the stationary prompt K/V and their own branch:
     (o_r [T][Hq][D], lse_r [Hq][T] float32)."""
+    T, Hq, Hkv, D, dt = _tree_sizes(q_r, k_p, offsets, "q_r", "k_p")
+    off = _offsets_list(offsets)
+    if _check_offsets(off) != T:
+        raise ValueError(f"q_r has {T} rows, offsets[-1] = {off[-1]}")
+    P = int(k_p.shape[0])
+    _expect("k_p", k_p, (P, Hkv, D), dt)
+    _expect("v_p", v_p, (P, Hkv, D), dt)
+    _expect("k_r", k_r, (T, Hkv, D), dt)
+    _expect("v_r", v_r, (T, Hkv, D), dt)
     dev = _check_tensors(("k_p", k_p), ("v_p", v_p), ("q_r", q_r), ("k_r", k_r), ("v_r", v_r))
-    T, Hq, D = q_r.shape
-    dims, keep = _dims(k_p.shape[0], _offsets_list(offsets), Hq, k_p.shape[1], D, scale, q_r.dtype)
+    dims, keep = _dims(P, off, Hq, Hkv, D, scale, dt)
     o_r = torch.empty_like(q_r)
     lse_r = torch.empty(Hq, T, dtype=torch.float32, device=dev)
     ws, n = _workspace(dims, _lib.AUGTREE_OP_REPLAY_FWD, dev)
@@ -96,11 +140,21 @@ def replay_fwd(k_p, v_p, q_r, k_r, v_r, offsets, scale: Optional[float] = None
 def replay_bwd(k_p, v_p, q_r, k_r, v_r, offsets, o_r, lse_r, do_r, scale: Optional[float] = None):
     """(dq_r, dk_r, dv_r, dk_p_acc, dv_p_acc): branch gradients and the branches' summed
     prompt K/V gradient in float32."""
+    T, Hq, Hkv, D, dt = _tree_sizes(q_r, k_p, offsets, "q_r", "k_p")
+    off = _offsets_list(offsets)
+    if _check_offsets(off) != T:
+        raise ValueError(f"q_r has {T} rows, offsets[-1] = {off[-1]}")
+    P = int(k_p.shape[0])
+    _expect("k_p", k_p, (P, Hkv, D), dt)
+    _expect("v_p", v_p, (P, Hkv, D), dt)
+    _expect("k_r", k_r, (T, Hkv, D), dt)
+    _expect("v_r", v_r, (T, Hkv, D), dt)
+    _expect("o_r", o_r, (T, Hq, D), dt)
+    _expect("lse_r", lse_r, (Hq, T), torch.float32)
+    _expect("do_r", do_r, (T, Hq, D), dt)
     dev = _check_tensors(("k_p", k_p), ("v_p", v_p), ("q_r", q_r), ("k_r", k_r), ("v_r", v_r),
                          ("o_r", o_r), ("lse_r", lse_r), ("do_r", do_r))
-    T, Hq, D = q_r.shape
-    P, Hkv = k_p.shape[0], k_p.shape[1]
-    dims, keep = _dims(P, _offsets_list(offsets), Hq, Hkv, D, scale, q_r.dtype)
+    dims, keep = _dims(P, off, Hq, Hkv, D, scale, dt)
     dq_r = torch.empty_like(q_r)
     dk_r = torch.empty_like(k_r)
     dv_r = torch.empty_like(v_r)
@@ -119,10 +173,20 @@ def prefill_bwd(q_p, k_p, v_p, o_p, lse_p, do_p, dk_p_acc=None, dv_p_acc=None,
                 scale: Optional[float] = None, offsets: Sequence[int] = (0, 1)):
     """(dq_p, dk_p, dv_p): prompt gradients including the branches' accumulated prompt
     K/V gradient when given."""
+    P, Hq, Hkv, D, dt = _tree_sizes(q_p, k_p, offsets, "q_p", "k_p")
+    _expect("k_p", k_p, (P, Hkv, D), dt)
+    _expect("v_p", v_p, (P, Hkv, D), dt)
+    _expect("o_p", o_p, (P, Hq, D), dt)
+    _expect("lse_p", lse_p, (Hq, P), torch.float32)
+    _expect("do_p", do_p, (P, Hq, D), dt)
+    if (dk_p_acc is None) != (dv_p_acc is None):
+        raise ValueError("dk_p_acc and dv_p_acc must both be given or both be None")
+    if dk_p_acc is not None:
+        _expect("dk_p_acc", dk_p_acc, (P, Hkv, D), torch.float32)
+        _expect("dv_p_acc", dv_p_acc, (P, Hkv, D), torch.float32)
     dev = _check_tensors(("q_p", q_p), ("k_p", k_p), ("v_p", v_p), ("o_p", o_p), ("lse_p", lse_p),
                          ("do_p", do_p), ("dk_p_acc", dk_p_acc), ("dv_p_acc", dv_p_acc))
-    P, Hq, D = q_p.shape
-    dims, keep = _dims(P, _offsets_list(offsets), Hq, k_p.shape[1], D, scale, q_p.dtype)
+    dims, keep = _dims(P, _offsets_list(offsets), Hq, Hkv, D, scale, dt)
     dq_p = torch.empty_like(q_p)
     dk_p = torch.empty_like(k_p)
     dv_p = torch.empty_like(v_p)
@@ -190,16 +254,52 @@ class Tree:
     def stream(self) -> int:
         return _stream(self.device)
 
+    def check(self, **named) -> None:
+        """Shape, dtype and device of the named tensors against this tree, before any call:
+        prompt rows P, branch rows T, query heads Hq, key/value heads Hkv, head_dim D.
+        Names: *_p / *_r tensors with q/o/do (Hq heads) or k/v (Hkv heads); lse_* and
+        rowdot_* [Hq][rows] float32; *_acc [P][Hkv][D] float32; o_part [T][Hq][D] and
+        lse_part [Hq][T] float32."""
+        f32 = torch.float32
+        for name, t in named.items():
+            if t is None:
+                continue
+            base = name.split("_")[0]
+            rows = self.P if name.endswith("_p") or name.endswith("_p_acc") else self.T
+            if name in ("o_part",):
+                _expect(name, t, (self.T, self.Hq, self.D), f32)
+            elif name in ("lse_part",):
+                _expect(name, t, (self.Hq, self.T), f32)
+            elif name.endswith("_acc"):
+                _expect(name, t, (self.P, self.Hkv, self.D), f32)
+            elif base in ("lse", "rowdot"):
+                _expect(name, t, (self.Hq, rows), f32)
+            elif base in ("q", "o", "do", "dq"):
+                _expect(name, t, (rows, self.Hq, self.D), self.dtype)
+            elif base in ("k", "v", "dk", "dv"):
+                _expect(name, t, (rows, self.Hkv, self.D), self.dtype)
+            else:
+                raise ValueError(f"unknown tensor name {name}")
+        for name, t in named.items():
+            if t is None:
+                continue
+            if not t.is_cuda or t.device != self.device:
+                raise ValueError(f"{name} must be on {self.device}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+
     def empty(self, *shape, dtype=None):
         return torch.empty(*shape, dtype=self.dtype if dtype is None else dtype, device=self.device)
 
     def workspace_bytes(self, op: int) -> int:
         return _lib.workspace_bytes(self.dims, op)
 
-    def workspace(self, op: int, ws=None):
-        """(pointer, bytes) of a workspace for operation `op`: `ws` when given (a uint8 GPU
-        tensor of at least the needed size), else a new one."""
-        n = self.workspace_bytes(op)
+    def workspace(self, op: int, ws=None, key_range=None):
+        """(pointer, bytes) of a workspace for operation `op` (over prompt keys key_range =
+        (begin, end) for the ops that take one): `ws` when given (a uint8 GPU tensor of at
+        least the needed size), else a new one."""
+        n = (self.workspace_bytes(op) if key_range is None
+             else _lib.range_workspace_bytes(self.dims, op, key_range[0], key_range[1]))
         if ws is None:
             ws = torch.empty(max(n, 1), dtype=torch.uint8, device=self.device)
         elif ws.numel() < n:
@@ -208,14 +308,21 @@ class Tree:
         return ws.data_ptr(), ws.numel()
 
 
+def _check_range(tr: "Tree", key_begin: int, key_end: int) -> None:
+    if not 0 <= key_begin < key_end <= tr.P:
+        raise ValueError(f"prompt key range [{key_begin}, {key_end}) not inside [0, {tr.P}) or empty")
+
+
 def replay_prompt_fwd(tr: Tree, k_p, v_p, q_r, key_begin: int = 0, key_end: Optional[int] = None,
                       out=None, ws=None):
     """Partial state (o_part float32 [T][Hq][D], lse_part [Hq][T]) of every branch row over
     prompt keys [key_begin, key_end)."""
     key_end = tr.P if key_end is None else key_end
+    _check_range(tr, key_begin, key_end)
     o, l = out if out is not None else (tr.empty(tr.T, tr.Hq, tr.D, dtype=torch.float32),
                                         tr.empty(tr.Hq, tr.T, dtype=torch.float32))
-    wp, wn = tr.workspace(_lib.AUGTREE_OP_REPLAY_PROMPT_FWD, ws)
+    tr.check(k_p=k_p, v_p=v_p, q_r=q_r, o_part=o, lse_part=l)
+    wp, wn = tr.workspace(_lib.AUGTREE_OP_REPLAY_PROMPT_FWD, ws, (key_begin, key_end))
     st = _lib.augtree_replay_prompt_fwd(tr.dims, k_p.data_ptr(), v_p.data_ptr(), q_r.data_ptr(), key_begin,
                                         key_end, o.data_ptr(), l.data_ptr(), wp, wn, tr.stream())
     _lib._check(st, "augtree_replay_prompt_fwd")
@@ -226,6 +333,7 @@ def replay_local_fwd(tr: Tree, q_r, k_r, v_r, out=None, ws=None):
     """Partial state of every branch row over its own branch (causal)."""
     o, l = out if out is not None else (tr.empty(tr.T, tr.Hq, tr.D, dtype=torch.float32),
                                         tr.empty(tr.Hq, tr.T, dtype=torch.float32))
+    tr.check(q_r=q_r, k_r=k_r, v_r=v_r, o_part=o, lse_part=l)
     wp, wn = tr.workspace(_lib.AUGTREE_OP_REPLAY_LOCAL_FWD, ws)
     st = _lib.augtree_replay_local_fwd(tr.dims, q_r.data_ptr(), k_r.data_ptr(), v_r.data_ptr(), o.data_ptr(),
                                        l.data_ptr(), wp, wn, tr.stream())
@@ -236,6 +344,11 @@ def replay_local_fwd(tr: Tree, q_r, k_r, v_r, out=None, ws=None):
 def merge_partials(tr: Tree, parts, out=None):
     """Exact log-sum-exp merge of [(o_part, lse_part), ...] -> (o_r dtype, lse_r)."""
     o, l = out if out is not None else (tr.empty(tr.T, tr.Hq, tr.D), tr.empty(tr.Hq, tr.T, dtype=torch.float32))
+    if not 1 <= len(parts) <= _lib.AUGTREE_MAX_PARTS:
+        raise ValueError(f"{len(parts)} parts, 1..{_lib.AUGTREE_MAX_PARTS} allowed")
+    for po, pl in parts:
+        tr.check(o_part=po, lse_part=pl)
+    tr.check(o_r=o, lse_r=l)
     st = _lib.augtree_merge_partials(tr.dims, [p[0].data_ptr() for p in parts], [p[1].data_ptr() for p in parts],
                                      o.data_ptr(), l.data_ptr(), tr.stream())
     _lib._check(st, "augtree_merge_partials")
@@ -244,8 +357,12 @@ def merge_partials(tr: Tree, parts, out=None):
 
 def row_dot(tr: Tree, o, d_o, out=None):
     """rowdot [Hq][rows] = sum_d dO * O for rows = o.shape[0] (P or T_R)."""
-    rows = o.shape[0]
+    rows = int(o.shape[0])
+    if rows not in (tr.P, tr.T):
+        raise ValueError(f"row_dot over {rows} rows: neither P={tr.P} nor T_R={tr.T}")
     r = out if out is not None else tr.empty(tr.Hq, rows, dtype=torch.float32)
+    sfx = "_p" if rows == tr.P else "_r"
+    tr.check(**{"o" + sfx: o, "do" + sfx: d_o, "rowdot" + sfx: r})
     st = _lib.augtree_row_dot(tr.dims, rows, o.data_ptr(), d_o.data_ptr(), r.data_ptr(), tr.stream())
     _lib._check(st, "augtree_row_dot")
     return r
@@ -256,10 +373,15 @@ def replay_prompt_bwd(tr: Tree, k_p, v_p, q_r, lse_r, rowdot_r, do_r, key_begin:
     """Rows [key_begin, key_end) of the branches' summed prompt K/V gradient (float32
     [P][Hkv][D] buffers, allocated when not given)."""
     key_end = tr.P if key_end is None else key_end
+    _check_range(tr, key_begin, key_end)
+    if (dk_acc is None) != (dv_acc is None):
+        raise ValueError("dk_acc and dv_acc must both be given or both be None")
     if dk_acc is None:
         dk_acc = tr.empty(tr.P, tr.Hkv, tr.D, dtype=torch.float32)
         dv_acc = tr.empty(tr.P, tr.Hkv, tr.D, dtype=torch.float32)
-    wp, wn = tr.workspace(_lib.AUGTREE_OP_REPLAY_PROMPT_BWD, ws)
+    tr.check(k_p=k_p, v_p=v_p, q_r=q_r, lse_r=lse_r, rowdot_r=rowdot_r, do_r=do_r, dk_acc=dk_acc,
+             dv_acc=dv_acc)
+    wp, wn = tr.workspace(_lib.AUGTREE_OP_REPLAY_PROMPT_BWD, ws, (key_begin, key_end))
     st = _lib.augtree_replay_prompt_bwd(tr.dims, k_p.data_ptr(), v_p.data_ptr(), q_r.data_ptr(), lse_r.data_ptr(),
                                         rowdot_r.data_ptr(), do_r.data_ptr(), key_begin, key_end, dk_acc.data_ptr(),
                                         dv_acc.data_ptr(), wp, wn, tr.stream())
@@ -269,6 +391,7 @@ def replay_prompt_bwd(tr: Tree, k_p, v_p, q_r, lse_r, rowdot_r, do_r, key_begin:
 
 def replay_local_bwd(tr: Tree, q_r, k_r, v_r, lse_r, rowdot_r, do_r, out=None, ws=None):
     dk, dv = out if out is not None else (torch.empty_like(k_r), torch.empty_like(v_r))
+    tr.check(q_r=q_r, k_r=k_r, v_r=v_r, lse_r=lse_r, rowdot_r=rowdot_r, do_r=do_r, dk_r=dk, dv_r=dv)
     wp, wn = tr.workspace(_lib.AUGTREE_OP_REPLAY_LOCAL_BWD, ws)
     st = _lib.augtree_replay_local_bwd(tr.dims, q_r.data_ptr(), k_r.data_ptr(), v_r.data_ptr(), lse_r.data_ptr(),
                                        rowdot_r.data_ptr(), do_r.data_ptr(), dk.data_ptr(), dv.data_ptr(),
@@ -279,6 +402,7 @@ def replay_local_bwd(tr: Tree, q_r, k_r, v_r, lse_r, rowdot_r, do_r, out=None, w
 
 def replay_dq(tr: Tree, k_p, v_p, q_r, k_r, v_r, lse_r, rowdot_r, do_r, out=None, ws=None):
     dq = out if out is not None else torch.empty_like(q_r)
+    tr.check(k_p=k_p, v_p=v_p, q_r=q_r, k_r=k_r, v_r=v_r, lse_r=lse_r, rowdot_r=rowdot_r, do_r=do_r, dq_r=dq)
     wp, wn = tr.workspace(_lib.AUGTREE_OP_REPLAY_DQ, ws)
     st = _lib.augtree_replay_dq(tr.dims, k_p.data_ptr(), v_p.data_ptr(), q_r.data_ptr(), k_r.data_ptr(),
                                 v_r.data_ptr(), lse_r.data_ptr(), rowdot_r.data_ptr(), do_r.data_ptr(),
@@ -289,6 +413,10 @@ def replay_dq(tr: Tree, k_p, v_p, q_r, k_r, v_r, lse_r, rowdot_r, do_r, out=None
 
 def prefill_kv_bwd(tr: Tree, q_p, k_p, v_p, lse_p, rowdot_p, do_p, dk_acc=None, dv_acc=None, out=None, ws=None):
     dk, dv = out if out is not None else (torch.empty_like(k_p), torch.empty_like(v_p))
+    if (dk_acc is None) != (dv_acc is None):
+        raise ValueError("dk_acc and dv_acc must both be given or both be None")
+    tr.check(q_p=q_p, k_p=k_p, v_p=v_p, lse_p=lse_p, rowdot_p=rowdot_p, do_p=do_p, dk_p_acc=dk_acc,
+             dv_p_acc=dv_acc, dk_p=dk, dv_p=dv)
     wp, wn = tr.workspace(_lib.AUGTREE_OP_PREFILL_KV_BWD, ws)
     st = _lib.augtree_prefill_kv_bwd(tr.dims, q_p.data_ptr(), k_p.data_ptr(), v_p.data_ptr(), lse_p.data_ptr(),
                                      rowdot_p.data_ptr(), do_p.data_ptr(), _ptr(dk_acc), _ptr(dv_acc),
@@ -299,6 +427,7 @@ def prefill_kv_bwd(tr: Tree, q_p, k_p, v_p, lse_p, rowdot_p, do_p, dk_acc=None, 
 
 def prefill_dq(tr: Tree, q_p, k_p, v_p, lse_p, rowdot_p, do_p, out=None, ws=None):
     dq = out if out is not None else torch.empty_like(q_p)
+    tr.check(q_p=q_p, k_p=k_p, v_p=v_p, lse_p=lse_p, rowdot_p=rowdot_p, do_p=do_p, dq_p=dq)
     wp, wn = tr.workspace(_lib.AUGTREE_OP_PREFILL_DQ, ws)
     st = _lib.augtree_prefill_dq(tr.dims, q_p.data_ptr(), k_p.data_ptr(), v_p.data_ptr(), lse_p.data_ptr(),
                                  rowdot_p.data_ptr(), do_p.data_ptr(), dq.data_ptr(), wp, wn, tr.stream())

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert _lib.abi_version() == 3
+    assert _lib.abi_version() == 4
     assert _lib.status_string(_lib.AUGTREE_OK) == "AUGTREE_OK"
     assert _lib.status_string(_lib.AUGTREE_ERR_WORKSPACE) == "AUGTREE_ERR_WORKSPACE"
     assert _lib.status_string(99) == "AUGTREE_ERR_UNKNOWN"
@@ -149,3 +149,47 @@ def test_last_error_is_per_thread():
     t.start()
     t.join()
     assert "prompt_len" in main_msg and seen == [""]
+
+
+@pytest.mark.parametrize("P,lens,Hq,Hkv", [
+    (32768, [1024] * 8, 8, 8),          # many key tiles, short branches: splits of 2..4 parts
+    (3000, [700, 45, 1210], 8, 2, ),    # few key tiles: splits up to 16 parts
+    (1500, [300, 200, 417], 4, 1),
+])
+def test_prompt_bwd_range_workspace_covers_every_range(P, lens, Hq, Hkv):
+    # The split count of the prompt K/V gradient depends on the number of keys in the range;
+    # for ranges that are not whole 256-key blocks it is clamped to the reserve, so no range
+    # needs more than the op-wide workspace. Walk every length (every start for the short
+    # prompts) on the host.
+    off = [0]
+    for r in lens:
+        off.append(off[-1] + r)
+    d, keep = _lib.make_dims(P, off, Hq, Hkv, 128, 128 ** -0.5, _lib.AUGTREE_BF16)
+    op = _lib.AUGTREE_OP_REPLAY_PROMPT_BWD
+    whole = _lib.workspace_bytes(d, op)
+    assert whole > 0
+    worst = 0
+    starts = range(P) if P <= 3000 else [0, 1, 255, 7423, 25345 - 1]
+    for kb in starts:
+        for ke in (range(kb + 1, P + 1) if P <= 3000 else [kb + 25345, P] if kb + 25345 <= P else [P]):
+            need = _lib.range_workspace_bytes(d, op, kb, ke)
+            assert 0 < need <= whole, (kb, ke, need, whole)
+            worst = max(worst, need)
+    if P == 32768:
+        # the length the advisor found (25345 keys: 3 parts) fits the op-wide reserve
+        for n in range(1, P + 1):
+            assert _lib.range_workspace_bytes(d, op, 0, n) <= whole, n
+    assert worst <= whole
+    # the fwd range workspace is the range's transposed V
+    assert _lib.range_workspace_bytes(d, _lib.AUGTREE_OP_REPLAY_PROMPT_FWD, 0, 65) == Hkv * 128 * 128 * 2
+    assert _lib.range_workspace_bytes(d, op, 5, 5) == 0
+    assert _lib.range_workspace_bytes(d, op, 0, P + 1) == 0
+
+
+def test_prompt_bwd_rejects_a_workspace_smaller_than_its_range_needs():
+    d, keep = _lib.make_dims(3000, [0, 700, 745, 1955], 8, 2, 128, 128 ** -0.5, _lib.AUGTREE_BF16)
+    op = _lib.AUGTREE_OP_REPLAY_PROMPT_BWD
+    for kb, ke in [(0, 3000), (13, 1777), (2999, 3000)]:
+        need = _lib.range_workspace_bytes(d, op, kb, ke)
+        st = _lib.augtree_replay_prompt_bwd(d, *([FAKE] * 6), kb, ke, FAKE, FAKE, FAKE, need - 1, None)
+        assert st == _lib.AUGTREE_ERR_WORKSPACE and "needed" in _lib.last_error()

@@ -87,5 +87,9 @@ def test_merge_of_one_part_is_a_copy_and_empty_key_range_rejected():
     assert torch.equal(ml, l)
     assert torch.equal(m, o.to(torch.bfloat16))
     from shared_prefix_attention_prompt_amd import _lib
-    with pytest.raises(_lib.AugtreeError):
+    with pytest.raises(ValueError):
         ops.replay_prompt_fwd(tr, t["k_p"], t["v_p"], t["q_r"], 10, 10)
+    # the library rejects it too, before any launch
+    st = _lib.augtree_replay_prompt_fwd(tr.dims, t["k_p"].data_ptr(), t["v_p"].data_ptr(), t["q_r"].data_ptr(),
+                                        10, 10, o.data_ptr(), l.data_ptr(), None, 0, None)
+    assert st == _lib.AUGTREE_ERR_INVALID_ARGUMENT
