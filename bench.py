@@ -155,6 +155,103 @@ def schedule(stages, nstreams):
     return p
 
 
+class Runner:
+    """One pass of the whole hot path over a tree (eleven single C-ABI steps, the identical
+    kernels of the four composite calls) on 1 or 3 streams, with every buffer allocated once.
+    ``step(ev)`` issues a pass; ``buf`` holds the outputs."""
+
+    def __init__(self, w, t, dev, nstreams: int = 1, nsh: int = 1):
+        import torch
+        from shared_prefix_attention_prompt_amd import _lib, ops
+        s = w.shape
+        self.shape = s
+        tr = ops.Tree(s.P, s.offsets, s.Hq, s.Hkv, s.D, s.torch_dtype, dev)
+        f32 = torch.float32
+        b = self.buf = {
+            "o_p": tr.empty(s.P, s.Hq, s.D), "lse_p": tr.empty(s.Hq, s.P, dtype=f32),
+            "oa": tr.empty(s.T, s.Hq, s.D, dtype=f32), "la": tr.empty(s.Hq, s.T, dtype=f32),
+            "ob": tr.empty(s.T, s.Hq, s.D, dtype=f32), "lb": tr.empty(s.Hq, s.T, dtype=f32),
+            "o_r": tr.empty(s.T, s.Hq, s.D), "lse_r": tr.empty(s.Hq, s.T, dtype=f32),
+            "rd_r": tr.empty(s.Hq, s.T, dtype=f32), "rd_p": tr.empty(s.Hq, s.P, dtype=f32),
+            "dk_acc": tr.empty(s.P, s.Hkv, s.D, dtype=f32), "dv_acc": tr.empty(s.P, s.Hkv, s.D, dtype=f32),
+            "dk_r": torch.empty_like(t["k_r"]), "dv_r": torch.empty_like(t["v_r"]),
+            "dq_r": torch.empty_like(t["q_r"]), "dk_p": torch.empty_like(t["k_p"]),
+            "dv_p": torch.empty_like(t["v_p"]), "dq_p": torch.empty_like(t["q_p"]),
+        }
+        cuts = [min(s.P, round(s.P * i / nsh / 256) * 256) for i in range(nsh)] + [s.P]
+        if any(q <= p for p, q in zip(cuts, cuts[1:])):
+            raise ValueError(f"--kv-shards {nsh}: the prompt of {s.P} keys cannot be cut into {nsh} non-empty "
+                             "ranges of whole 256-key blocks")
+        self.cuts = cuts
+        shard_bufs = [(tr.empty(s.T, s.Hq, s.D, dtype=f32), tr.empty(s.Hq, s.T, dtype=f32)) for _ in range(nsh - 1)]
+        nws = max(_lib.workspace_bytes(tr.dims, op) for op in range(11))
+        main = torch.cuda.current_stream(dev)
+        self.nstreams = nstreams
+        streams = [main] if nstreams == 1 else [torch.cuda.Stream(dev) for _ in range(3)]
+        wss = [torch.empty(max(nws, 256), dtype=torch.uint8, device=dev) for _ in streams]
+        run = {
+            "prefill_fwd": lambda ws: _lib._check(_lib.augtree_prefill_fwd(
+                tr.dims, t["q_p"].data_ptr(), t["k_p"].data_ptr(), t["v_p"].data_ptr(), b["o_p"].data_ptr(),
+                b["lse_p"].data_ptr(), ws.data_ptr(), ws.numel(), tr.stream()), "augtree_prefill_fwd"),
+            "replay_prompt_fwd": lambda ws: [ops.replay_prompt_fwd(
+                tr, t["k_p"], t["v_p"], t["q_r"], cuts[i], cuts[i + 1],
+                out=(b["oa"], b["la"]) if i == 0 else shard_bufs[i - 1], ws=ws) for i in range(nsh)],
+            "replay_local_fwd": lambda ws: ops.replay_local_fwd(tr, t["q_r"], t["k_r"], t["v_r"],
+                                                                out=(b["ob"], b["lb"]), ws=ws),
+            "merge": lambda ws: ops.merge_partials(tr, [(b["oa"], b["la"])] + shard_bufs + [(b["ob"], b["lb"])],
+                                                   out=(b["o_r"], b["lse_r"])),
+            "row_dot_r": lambda ws: ops.row_dot(tr, b["o_r"], t["do_r"], out=b["rd_r"]),
+            "replay_prompt_bwd": lambda ws: [ops.replay_prompt_bwd(
+                tr, t["k_p"], t["v_p"], t["q_r"], b["lse_r"], b["rd_r"], t["do_r"], cuts[i], cuts[i + 1],
+                dk_acc=b["dk_acc"], dv_acc=b["dv_acc"], ws=ws) for i in range(nsh)],
+            "replay_local_bwd": lambda ws: ops.replay_local_bwd(
+                tr, t["q_r"], t["k_r"], t["v_r"], b["lse_r"], b["rd_r"], t["do_r"], out=(b["dk_r"], b["dv_r"]),
+                ws=ws),
+            "replay_dq": lambda ws: ops.replay_dq(tr, t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], b["lse_r"],
+                                                  b["rd_r"], t["do_r"], out=b["dq_r"], ws=ws),
+            "row_dot_p": lambda ws: ops.row_dot(tr, b["o_p"], t["do_p"], out=b["rd_p"]),
+            "prefill_kv_bwd": lambda ws: ops.prefill_kv_bwd(
+                tr, t["q_p"], t["k_p"], t["v_p"], b["lse_p"], b["rd_p"], t["do_p"], b["dk_acc"], b["dv_acc"],
+                out=(b["dk_p"], b["dv_p"]), ws=ws),
+            "prefill_dq": lambda ws: ops.prefill_dq(tr, t["q_p"], t["k_p"], t["v_p"], b["lse_p"], b["rd_p"],
+                                                    t["do_p"], out=b["dq_p"], ws=ws),
+        }
+        self.stages = STAGES if s.backward else STAGES[:4]
+        plan = schedule(self.stages, nstreams)
+        self._torch, self._main, self._streams, self._wss, self._run, self._plan = torch, main, streams, wss, run, plan
+
+    def step(self, ev=None):
+        """One pass of the whole path. ev: per-stage (start, end) timing events, recorded on
+        the stream each stage runs on."""
+        torch, main, streams = self._torch, self._main, self._streams
+        if self.nstreams > 1:
+            fork = torch.cuda.Event()
+            fork.record(main)
+            for x in streams:
+                x.wait_event(fork)
+        marks = {}
+        for kind, si, name in self._plan:
+            st = streams[si]
+            if kind == "wait":
+                st.wait_event(marks[name])
+                continue
+            if kind == "mark":
+                marks[name] = torch.cuda.Event()
+                marks[name].record(st)
+                continue
+            with torch.cuda.stream(st):
+                if ev is not None:
+                    ev[name][0].record(st)
+                self._run[name](self._wss[si])
+                if ev is not None:
+                    ev[name][1].record(st)
+        if self.nstreams > 1:
+            for x in streams:
+                j = torch.cuda.Event()
+                j.record(x)
+                main.wait_event(j)
+
+
 def kernel_source_digest():
     """sha256 over the HIP sources, so stored counter readings are only reported for the
     kernels they were taken on."""
@@ -233,107 +330,36 @@ def main() -> int:
     print(f"# inputs for config {cfg} ready in {time.perf_counter() - t_gen:.1f} s "
           f"(P={s.P}, T_R={s.T}, G={s.G}, Hq={s.Hq}, Hkv={s.Hkv}, D={s.D})", file=sys.stderr, flush=True)
 
-    tr = ops.Tree(s.P, s.offsets, s.Hq, s.Hkv, s.D, s.torch_dtype, dev)
-    f32 = torch.float32
-    buf = {
-        "o_p": tr.empty(s.P, s.Hq, s.D), "lse_p": tr.empty(s.Hq, s.P, dtype=f32),
-        "oa": tr.empty(s.T, s.Hq, s.D, dtype=f32), "la": tr.empty(s.Hq, s.T, dtype=f32),
-        "ob": tr.empty(s.T, s.Hq, s.D, dtype=f32), "lb": tr.empty(s.Hq, s.T, dtype=f32),
-        "o_r": tr.empty(s.T, s.Hq, s.D), "lse_r": tr.empty(s.Hq, s.T, dtype=f32),
-        "rd_r": tr.empty(s.Hq, s.T, dtype=f32), "rd_p": tr.empty(s.Hq, s.P, dtype=f32),
-        "dk_acc": tr.empty(s.P, s.Hkv, s.D, dtype=f32), "dv_acc": tr.empty(s.P, s.Hkv, s.D, dtype=f32),
-        "dk_r": torch.empty_like(t["k_r"]), "dv_r": torch.empty_like(t["v_r"]),
-        "dq_r": torch.empty_like(t["q_r"]), "dk_p": torch.empty_like(t["k_p"]),
-        "dv_p": torch.empty_like(t["v_p"]), "dq_p": torch.empty_like(t["q_p"]),
-    }
     nsh = args.kv_shards
-    cuts = [min(s.P, round(s.P * i / nsh / 256) * 256) for i in range(nsh)] + [s.P]
-    if any(b <= a for a, b in zip(cuts, cuts[1:])):
-        print(f"--kv-shards {nsh}: the prompt of {s.P} keys cannot be cut into {nsh} non-empty "
-              "ranges of whole 256-key blocks", file=sys.stderr)
-        return 2
-    shard_bufs = [(tr.empty(s.T, s.Hq, s.D, dtype=f32), tr.empty(s.Hq, s.T, dtype=f32)) for _ in range(nsh - 1)]
-    nws = max(_lib.workspace_bytes(tr.dims, op) for op in range(11))
-    main = torch.cuda.current_stream(dev)
     nstreams = args.streams if args.streams > 0 else (3 if small_grid(s) else 1)
-    streams = [main] if nstreams == 1 else [torch.cuda.Stream(dev) for _ in range(3)]
-    wss = [torch.empty(max(nws, 256), dtype=torch.uint8, device=dev) for _ in streams]
-    b = buf
-    run = {
-        "prefill_fwd": lambda ws: _lib._check(_lib.augtree_prefill_fwd(
-            tr.dims, t["q_p"].data_ptr(), t["k_p"].data_ptr(), t["v_p"].data_ptr(), b["o_p"].data_ptr(),
-            b["lse_p"].data_ptr(), ws.data_ptr(), ws.numel(), tr.stream()), "augtree_prefill_fwd"),
-        "replay_prompt_fwd": lambda ws: [ops.replay_prompt_fwd(
-            tr, t["k_p"], t["v_p"], t["q_r"], cuts[i], cuts[i + 1],
-            out=(b["oa"], b["la"]) if i == 0 else shard_bufs[i - 1], ws=ws) for i in range(nsh)],
-        "replay_local_fwd": lambda ws: ops.replay_local_fwd(tr, t["q_r"], t["k_r"], t["v_r"],
-                                                            out=(b["ob"], b["lb"]), ws=ws),
-        "merge": lambda ws: ops.merge_partials(tr, [(b["oa"], b["la"])] + shard_bufs + [(b["ob"], b["lb"])],
-                                               out=(b["o_r"], b["lse_r"])),
-        "row_dot_r": lambda ws: ops.row_dot(tr, b["o_r"], t["do_r"], out=b["rd_r"]),
-        "replay_prompt_bwd": lambda ws: [ops.replay_prompt_bwd(
-            tr, t["k_p"], t["v_p"], t["q_r"], b["lse_r"], b["rd_r"], t["do_r"], cuts[i], cuts[i + 1],
-            dk_acc=b["dk_acc"], dv_acc=b["dv_acc"], ws=ws) for i in range(nsh)],
-        "replay_local_bwd": lambda ws: ops.replay_local_bwd(
-            tr, t["q_r"], t["k_r"], t["v_r"], b["lse_r"], b["rd_r"], t["do_r"], out=(b["dk_r"], b["dv_r"]), ws=ws),
-        "replay_dq": lambda ws: ops.replay_dq(tr, t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], b["lse_r"],
-                                              b["rd_r"], t["do_r"], out=b["dq_r"], ws=ws),
-        "row_dot_p": lambda ws: ops.row_dot(tr, b["o_p"], t["do_p"], out=b["rd_p"]),
-        "prefill_kv_bwd": lambda ws: ops.prefill_kv_bwd(
-            tr, t["q_p"], t["k_p"], t["v_p"], b["lse_p"], b["rd_p"], t["do_p"], b["dk_acc"], b["dv_acc"],
-            out=(b["dk_p"], b["dv_p"]), ws=ws),
-        "prefill_dq": lambda ws: ops.prefill_dq(tr, t["q_p"], t["k_p"], t["v_p"], b["lse_p"], b["rd_p"],
-                                                t["do_p"], out=b["dq_p"], ws=ws),
-    }
-    stages = STAGES if s.backward else STAGES[:4]
-    plan = schedule(stages, nstreams)
-
-    def step(ev=None):
-        """One pass of the whole path. ev: per-stage (start, end) timing events, recorded on
-        the stream each stage runs on."""
-        if nstreams > 1:
-            fork = torch.cuda.Event()
-            fork.record(main)
-            for x in streams:
-                x.wait_event(fork)
-        marks = {}
-        for kind, si, name in plan:
-            st = streams[si]
-            if kind == "wait":
-                st.wait_event(marks[name])
-                continue
-            if kind == "mark":
-                marks[name] = torch.cuda.Event()
-                marks[name].record(st)
-                continue
-            with torch.cuda.stream(st):
-                if ev is not None:
-                    ev[name][0].record(st)
-                run[name](wss[si])
-                if ev is not None:
-                    ev[name][1].record(st)
-        if nstreams > 1:
-            for x in streams:
-                j = torch.cuda.Event()
-                j.record(x)
-                main.wait_event(j)
+    try:
+        runner = Runner(w, t, dev, nstreams, nsh)
+    except ValueError as e:
+        print(str(e), file=sys.stderr)
+        return 2
+    stages, step = runner.stages, runner.step
+    main = torch.cuda.current_stream(dev)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     events = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in stages}
               for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    # one event per step boundary on the main stream (every stream joins it at each step's
+    # end): the K steps' total time, and the median step
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    start.record(main)
+    marks[0].record(main)
     for i in range(args.steps):
         step(events[i])
-    end.record(main)
+        marks[i + 1].record(main)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = start.elapsed_time(end) / args.steps
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    ms_per_step = marks[0].elapsed_time(marks[-1]) / args.steps
+    ms_median = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
+        step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
 
     stage_ms = {}
     for name in stages:
@@ -380,6 +406,8 @@ def main() -> int:
     line = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(ms_median, 4), "ms_per_step_min": round(step_ms[0], 4),
+        "ms_per_step_max": round(step_ms[-1], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": s.dtype,
         "data": "synthetic", "pct_bf16_peak": round(100 * tflops / peak, 2),
         "config": {"workload": workload_name(cfg), "P": s.P, "G": s.G, "branch_lens": list(s.lens),

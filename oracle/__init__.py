@@ -10,6 +10,6 @@ Every function here is pinned by the ``-m "not gpu"`` tests in ``tests/test_orac
 tree mask, finite differences, and invariants of the mathematics).
 """
 from .flat_attention import (rows_attention, flattened_tree_attention,  # noqa: F401
-                             flattened_sampled_rows, branch_response_grads)
+                             flattened_sampled_rows, branch_response_grads, prompt_key_grads)
 from .flat_chain import flattened_chain  # noqa: F401
 from .assign import brute_force_assign, greedy_assign, grid_cost  # noqa: F401

@@ -42,7 +42,7 @@ import torch
 f64 = torch.float64
 
 __all__ = ["rows_attention", "flattened_tree_attention", "flattened_sampled_rows",
-           "branch_response_grads"]
+           "branch_response_grads", "prompt_key_grads"]
 
 
 def rows_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, counts: torch.Tensor,
@@ -316,3 +316,85 @@ def branch_response_grads(q_p, k_p, v_p, q_r, k_r, v_r, offsets, branch: int, do
             out["o_r"][r0:r1, a] = o
             out["lse_r"][a, r0:r1] = lse
     return out
+
+
+def _selected_key_grads(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, counts: torch.Tensor,
+                        scale: float, do: torch.Tensor, keys: torch.Tensor):
+    """Contribution of a block of query rows to dK and dV of the key positions ``keys``.
+
+    Same arithmetic as :func:`rows_attention` (two-pass softmax over each row's visible keys
+    0 .. counts[j]-1, rowdot in its plain form sum_j P_j dP_j), with the backward evaluated only
+    for the selected key columns: dS = P o (dP - rowdot), dK = scale dS^T Q, dV = P^T dO.
+    """
+    L = k.shape[0]
+    s = (q @ k.T) * scale
+    hidden = torch.arange(L)[None, :] >= counts[:, None]
+    s = s.masked_fill(hidden, float("-inf"))
+    m = s.max(dim=1).values
+    lse = m + torch.log(torch.exp(s - m[:, None]).sum(dim=1))
+    p = torch.exp(s - lse[:, None])
+    dp = do @ v.T
+    rowdot = (p * dp).sum(dim=1)
+    pj = p[:, keys]
+    dsj = pj * (dp[:, keys] - rowdot[:, None])
+    return (dsj.T @ q) * scale, pj.T @ do
+
+
+def prompt_key_grads(q_p, k_p, v_p, q_r, k_r, v_r, offsets, keys: Sequence[int], do_p, do_r,
+                     kv_heads: Optional[Iterable[int]] = None, scale: Optional[float] = None,
+                     slab: int = 256) -> Dict[str, torch.Tensor]:
+    """dK and dV of selected prompt keys: the total prompt-key gradient of §3.2 (the prompt
+    queries' own part plus, by the equation after Eq. 1, the sum over branches of each branch
+    loss's gradient), for the selected key/value heads (all query heads of each group).
+
+    A prompt key j is seen by prompt rows r >= j and by every response row of every branch
+    (in each flattened copy (P, R_i) it is a prefix key). Each row is normalised over its own
+    whole flattened sequence (two-pass softmax), so every row still runs over all its visible
+    keys; only the gradient columns of the selected keys are formed. The prompt rows' upstream
+    gradient is taken whole on copy 0 (split weights (1, 0, ..., 0); by linearity every split
+    with weights summing to 1 gives the same gradient, which the pins check).
+
+    Returns dk_p, dv_p [n_keys][n_kv][D] (fp64), ``keys`` and ``kv_heads``.
+    """
+    off = [int(x) for x in (offsets.tolist() if torch.is_tensor(offsets) else offsets)]
+    P, Hq, D = q_p.shape
+    Hkv = k_p.shape[1]
+    G = len(off) - 1
+    group = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / D ** 0.5
+    kvs = list(range(Hkv)) if kv_heads is None else [int(g) for g in kv_heads]
+    J = torch.tensor(sorted(set(int(j) for j in keys)), dtype=torch.long)
+    assert len(J) and int(J.min()) >= 0 and int(J.max()) < P
+    dk = torch.zeros(len(J), len(kvs), D, dtype=f64)
+    dv = torch.zeros(len(J), len(kvs), D, dtype=f64)
+    for b, g in enumerate(kvs):
+        kp_g, vp_g = _as64(k_p[:, g]), _as64(v_p[:, g])
+        kr_g, vr_g = _as64(k_r[:, g]), _as64(v_r[:, g])
+        for h in range(g * group, (g + 1) * group):
+            qp_h, dop_h = _as64(q_p[:, h]), _as64(do_p[:, h])
+            # prompt rows (copy 0): row r sees prompt keys 0..r
+            for r0 in range(0, P, slab):
+                r1 = min(P, r0 + slab)
+                sel = (J < r1).nonzero().flatten()
+                if len(sel) == 0:
+                    continue
+                gk, gv = _selected_key_grads(qp_h[r0:r1], kp_g[:r1], vp_g[:r1], torch.arange(r0, r1) + 1,
+                                             scale, dop_h[r0:r1], J[sel])
+                dk[sel, b] += gk
+                dv[sel, b] += gv
+            # response rows of every copy: row t of branch i sees all prompt keys and its
+            # branch's keys up to itself
+            qr_h, dor_h = _as64(q_r[:, h]), _as64(do_r[:, h])
+            for i in range(G):
+                k = _branch_seq(kp_g, kr_g, off, i)
+                v = _branch_seq(vp_g, vr_g, off, i)
+                R = off[i + 1] - off[i]
+                for t0 in range(0, R, slab):
+                    t1 = min(R, t0 + slab)
+                    gk, gv = _selected_key_grads(qr_h[off[i] + t0:off[i] + t1], k[:P + t1], v[:P + t1],
+                                                 P + torch.arange(t0, t1) + 1, scale,
+                                                 dor_h[off[i] + t0:off[i] + t1], J)
+                    dk[:, b] += gk
+                    dv[:, b] += gv
+    return {"dk_p": dk, "dv_p": dv, "keys": J, "kv_heads": torch.tensor(kvs)}

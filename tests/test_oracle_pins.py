@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from oracle import (branch_response_grads, flattened_sampled_rows, flattened_tree_attention,
-                    rows_attention)
+                    prompt_key_grads, rows_attention)
 from tests.tree_reference import tree_attention
 from workloads import make_inputs, make_shape
 
@@ -273,6 +273,35 @@ def test_branch_response_grads_match_library_tree_attention():
     assert torch.allclose(b["dv_r"], ref["dv_r"][rows][:, [1]], atol=1e-12)
     assert torch.allclose(b["dq_r"], ref["dq_r"][rows][:, [2, 3]], atol=1e-12)
     assert torch.allclose(b["o_r"], ref["o_r"][rows][:, [2, 3]], atol=1e-12)
+
+
+@pytest.mark.parametrize("P,lens,Hq,Hkv,D,kv,keys,slab,seed", [
+    (13, [5, 9, 1], 4, 2, 8, [1], [0, 3, 7, 12], 4, 121),
+    (20, [1, 30], 2, 2, 16, [0, 1], [19, 0, 1, 10], 3, 122),
+    (9, [4, 4, 4, 4], 6, 2, 8, [1], list(range(9)), 256, 123),
+    (33, [2, 40, 3], 8, 1, 8, [0], [0, 16, 31, 32], 5, 124),
+])
+def test_prompt_key_grads_match_library_tree_attention(P, lens, Hq, Hkv, D, kv, keys, slab, seed):
+    # the selected prompt keys' total gradient (prompt rows + every branch, all query heads of
+    # the group) equals the library attention routine's autograd gradient under the tree mask
+    w = _inputs(P, lens, Hq, Hkv, D, seed)
+    ref = tree_attention(w.q_p, w.k_p, w.v_p, w.q_r, w.k_r, w.v_r, w.offsets, do_p=w.do_p, do_r=w.do_r)
+    g = prompt_key_grads(w.q_p, w.k_p, w.v_p, w.q_r, w.k_r, w.v_r, w.offsets, keys, w.do_p, w.do_r,
+                         kv_heads=kv, slab=slab)
+    J = sorted(set(keys))
+    assert g["keys"].tolist() == J
+    assert torch.allclose(g["dk_p"], ref["dk_p"][J][:, kv], atol=1e-12), (g["dk_p"] - ref["dk_p"][J][:, kv]).abs().max()
+    assert torch.allclose(g["dv_p"], ref["dv_p"][J][:, kv], atol=1e-12)
+
+
+def test_prompt_key_grads_detect_a_key_off_by_one():
+    # a gradient of key j reported for key j+1 (a misrouted row) fails the comparison above:
+    # neighbouring keys' gradients differ by far more than the tolerance
+    w = _inputs(13, [5, 9, 1], 4, 2, 8, 121)
+    g = prompt_key_grads(w.q_p, w.k_p, w.v_p, w.q_r, w.k_r, w.v_r, w.offsets, list(range(13)), w.do_p,
+                         w.do_r, kv_heads=[0])
+    assert float((g["dk_p"][1:] - g["dk_p"][:-1]).abs().amax(dim=(1, 2)).min()) > 1e-3
+    assert float((g["dv_p"][1:] - g["dv_p"][:-1]).abs().amax(dim=(1, 2)).min()) > 1e-3
 
 
 def test_rows_attention_single_visible_key():

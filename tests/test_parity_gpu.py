@@ -7,16 +7,19 @@ flattened oracle are checked on one full key/value group, on sampled rows (a row
 and dQ depend only on its own flattened sequence), on one branch's own K/V gradients, and
 on sum rules that hold at any size.
 """
+import os
 import random
 
+import numpy as np
 import pytest
 import torch
 
 from oracle import branch_response_grads, flattened_sampled_rows, flattened_tree_attention
-from tests.gpu_run import compare, config_inputs, log, run_path, sum_rules, upload
+from tests.gpu_run import NAMES, compare, config_inputs, log, run_path, sum_rules, upload
 from workloads import make_inputs, make_shape
 
 pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
 
 ALL = ["o_p", "lse_p", "o_r", "lse_r", "dq_p", "dk_p", "dv_p", "dq_r", "dk_r", "dv_r"]
 
@@ -39,7 +42,7 @@ def _full_check(w, keys, kv_heads=None, abs_scale=False):
         else:
             g = g[:, qh]
         compare(k, g, ref[k], w.shape.dtype, report, abs_scale=abs_scale)
-    log("  " + ", ".join(f"{n} {e:.1e}/{r:.1e}" for n, e, r, _ in report))
+    log("  " + ", ".join(f"{n} {e:.1e} (plain {p:.1e})/{r:.1e}" for n, e, r, _, p in report))
     return out
 
 
@@ -105,7 +108,26 @@ def test_config3_bitwise_repeatable():
         assert torch.equal(a[k], b[k]), k
 
 
-def _sampled_check(cfg, n_prompt_rows, rows_per_branch, grad_branch_kv=0, sample_seed=None):
+def _golden_prompt_keys(cfg, w, out, report):
+    """Element-wise dK_P / dV_P at the stored sampled prompt keys (written by
+    tests/golden/make_prompt_key_grads.py from the oracle alone)."""
+    path = os.path.join(HERE, "golden", f"prompt_key_grads_cfg{cfg}.npz")
+    g = np.load(path, allow_pickle=False)
+    fp = np.array([float(getattr(w, n).double().sum()) for n in NAMES] +
+                  [float(getattr(w, n).double().abs().sum()) for n in NAMES])
+    assert np.allclose(fp, g["fingerprint"], rtol=1e-9, atol=1e-6), "inputs differ from the stored ones"
+    assert list(g["offsets"]) == list(w.shape.offsets)
+    keys = torch.from_numpy(g["keys"].astype(np.int64)).to(out["dk_p"].device)
+    kv = int(g["kv_head"])
+    log(f"  prompt keys: {len(keys)} of kv head {kv}, every 256-key block")
+    compare("dk_p(keys)", out["dk_p"][keys, kv], torch.from_numpy(g["dk_p"]).double(), w.shape.dtype, report)
+    compare("dv_p(keys)", out["dv_p"][keys, kv], torch.from_numpy(g["dv_p"]).double(), w.shape.dtype, report)
+    # the fp32 branch sums alone must not be what is compared: they differ from the totals
+    assert not torch.allclose(out["dk_p_acc"][keys, kv].double().cpu(), torch.from_numpy(g["dk_p"]).double(),
+                              atol=2e-2)
+
+
+def _sampled_check(cfg, n_prompt_rows, rows_per_branch, grad_branch_kv=0, sample_seed=None, golden_keys=False):
     w = config_inputs(cfg)
     s = w.shape
     log(f"config {cfg}: P={s.P} T={s.T} lens={list(s.lens)}")
@@ -137,16 +159,21 @@ def _sampled_check(cfg, n_prompt_rows, rows_per_branch, grad_branch_kv=0, sample
     sl = slice(off[b], off[b + 1])
     compare("dk_r(branch)", out["dk_r"][sl, [grad_branch_kv]], br["dk_r"], s.dtype, report)
     compare("dv_r(branch)", out["dv_r"][sl, [grad_branch_kv]], br["dv_r"], s.dtype, report)
-    log("  " + ", ".join(f"{n} {e:.1e}/{r:.1e}" for n, e, r, _ in report))
+    if golden_keys:
+        _golden_prompt_keys(cfg, w, out, report)
+    log(f"  {len(prow)} prompt rows, {len(rrow)} branch rows")
+    log("  " + ", ".join(f"{n} {e:.1e} (plain {p:.1e})/{r:.1e}" for n, e, r, _, p in report))
     e_v, e_k = sum_rules(w, out)
     log(f"  sum rules: dV {e_v:.2e}, dK {e_k:.2e}")
     assert e_v < 1e-2 and e_k < 1e-2
 
 
-# Two disjointly seeded samples of about 290 rows each (over 512 rows in all, spread over the
-# prompt and every branch, first and last rows included), each within the per-test time limit.
+# Two disjointly seeded samples of about 290 rows each per workload (over 512 rows in all,
+# spread over the prompt and every branch, first and last rows included), each within the
+# per-test time limit; the first also checks 4096 stored prompt keys of one kv head element by
+# element (the branch-summed prompt gradient plus the prefill part, §3.2).
 def test_config4_sampled_rows_branch_grads_sum_rules():
-    _sampled_check(4, n_prompt_rows=40, rows_per_branch=28)
+    _sampled_check(4, n_prompt_rows=40, rows_per_branch=28, golden_keys=True)
 
 
 def test_config4_more_sampled_rows():
@@ -154,7 +181,20 @@ def test_config4_more_sampled_rows():
 
 
 def test_config5_sampled_rows_branch_grads_sum_rules():
-    _sampled_check(5, n_prompt_rows=8, rows_per_branch=6, grad_branch_kv=7)
+    _sampled_check(5, n_prompt_rows=24, rows_per_branch=14, grad_branch_kv=7, golden_keys=True)
+
+
+def test_config5_more_sampled_rows():
+    _sampled_check(5, n_prompt_rows=24, rows_per_branch=14, grad_branch_kv=2, sample_seed=5005)
+
+
+def test_long_prompt_lockstep_chunks_full_kv_head():
+    # P = 16384 with 8 kv heads: the prefill K/V gradient walk is cut into two 8192-row chunks
+    # run chunk by chunk (the long-prompt path), and the prompt K/V gradient over the branches
+    # runs unsplit (512 workgroups); every prompt key of kv head 0 is compared, so a chunk
+    # partial added to the wrong key row fails.
+    w = make_inputs(make_shape(16384, [5, 9], 8, 8, 128, dtype="bf16"), seed=16384)
+    _full_check(w, ALL, kv_heads=[0])
 
 
 # Group-size / prompt:response-ratio sweep trees at full size (28 query / 4 key-value heads):
