@@ -36,8 +36,9 @@
  * Errors: arguments are validated on the host before anything is enqueued. On an error
  * the call returns a non-zero status and enqueues nothing, except AUGTREE_ERR_HIP, which
  * may follow a partial enqueue. augtree_last_error() then describes the failure (per
- * thread). No C++ exception crosses this interface. The library holds no mutable global
- * state and may be called from several host threads.
+ * thread). No C++ exception crosses this interface. The library may be called from several
+ * host threads; its only mutable global state is the per-device address table of the static
+ * scratch of augtree_replay_fwd_noalloc (filled once per device, under a lock).
  *
  * Results are bitwise reproducible for identical inputs and dims: no floating-point
  * atomics are used anywhere; every reduction runs in a fixed order.
@@ -146,6 +147,28 @@ augtree_status augtree_prefill_bwd(const augtree_dims *dims, const void *q_p, co
                                    const void *do_p, const float *dk_p_acc,
                                    const float *dv_p_acc, void *dq_p, void *dk_p, void *dv_p,
                                    void *ws, size_t ws_bytes, void *stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. Same computation, kernels and results as
+ * augtree_replay_fwd (bitwise), but the workspace is a static array of the library's code
+ * object, AUGTREE_NOALLOC_SCRATCH_BYTES per GPU, reserved on each GPU the library runs on
+ * until the process ends. The caller still passes inputs and outputs (device pointers, as
+ * for augtree_replay_fwd); the call allocates and frees nothing. The current device
+ * (hipGetDevice) must be the device of the buffers and of `stream`; its scratch address is
+ * looked up on the first call on that device.
+ * Every call on one GPU shares that GPU's scratch, and the scratch keeps the last call's
+ * contents (nothing in it needs to start at zero: every byte read is first written by the
+ * same call). Calls that overlap in time on one GPU (several streams, or several host
+ * threads) race on the scratch and give undefined results: serialise them.
+ * Errors: as augtree_replay_fwd; AUGTREE_ERR_WORKSPACE (before anything is enqueued) when
+ * the tree needs more scratch than AUGTREE_NOALLOC_SCRATCH_BYTES, i.e. when
+ * augtree_workspace_bytes(dims, AUGTREE_OP_REPLAY_FWD) exceeds it (about 2*T_R*Hq*(D+1)*4
+ * bytes plus two transposed V copies: T_R*Hq up to about 2.5e5 at D = 128). */
+#define AUGTREE_NOALLOC_SCRATCH_BYTES (256u << 20)
+augtree_status augtree_replay_fwd_noalloc(const augtree_dims *dims, const void *k_p,
+                                          const void *v_p, const void *q_r, const void *k_r,
+                                          const void *v_r, void *o_r, float *lse_r,
+                                          void *stream);
 
 /* ---------------------------------------------------------------------------------------
  * Single steps. The four calls above are compositions of these (each launches one kernel,

@@ -33,12 +33,14 @@ AUGTREE_OP_PREFILL_DQ = 10
 AUGTREE_MAX_BRANCHES = 128
 AUGTREE_MAX_PARTS = 8
 AUGTREE_ASSIGN_EXACT_MAX = 16
+AUGTREE_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 ENTRY_POINTS = ["augtree_prefill_fwd", "augtree_replay_fwd", "augtree_replay_bwd",
                 "augtree_prefill_bwd", "augtree_replay_prompt_fwd", "augtree_replay_local_fwd",
                 "augtree_merge_partials", "augtree_row_dot", "augtree_replay_prompt_bwd",
                 "augtree_replay_local_bwd", "augtree_replay_dq", "augtree_prefill_kv_bwd",
-                "augtree_prefill_dq", "augtree_assign_units", "augtree_workspace_bytes",
+                "augtree_prefill_dq", "augtree_assign_units", "augtree_replay_fwd_noalloc",
+                "augtree_workspace_bytes",
                 "augtree_range_workspace_bytes",
                 "augtree_status_string", "augtree_last_error", "augtree_abi_version"]
 
@@ -88,7 +90,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.augtree_prefill_kv_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.augtree_prefill_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.augtree_assign_units.argtypes = [vp, i32, i32, i32, i32, vp, vp]
-    for name in ENTRY_POINTS[:14]:
+    lib.augtree_replay_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    for name in ENTRY_POINTS[:15]:
         getattr(lib, name).restype = st
     lib.augtree_workspace_bytes.argtypes = [P, ctypes.c_int]
     lib.augtree_workspace_bytes.restype = sz
@@ -164,6 +167,10 @@ def augtree_prefill_bwd(dims, q_p, k_p, v_p, o_p, lse_p, do_p, dk_p_acc, dv_p_ac
                         dv_p, ws, ws_bytes, stream) -> int:
     return load().augtree_prefill_bwd(ctypes.byref(dims), q_p, k_p, v_p, o_p, lse_p, do_p, dk_p_acc,
                                       dv_p_acc, dq_p, dk_p, dv_p, ws, ws_bytes, stream)
+
+
+def augtree_replay_fwd_noalloc(dims, k_p, v_p, q_r, k_r, v_r, o_r, lse_r, stream) -> int:
+    return load().augtree_replay_fwd_noalloc(ctypes.byref(dims), k_p, v_p, q_r, k_r, v_r, o_r, lse_r, stream)
 
 
 def augtree_replay_prompt_fwd(dims, k_p, v_p, q_r, key_begin, key_end, o_part, lse_part, ws, ws_bytes,

@@ -6,10 +6,16 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/augtree.h"
 #include "kernels.hpp"
+
+// Scratch of augtree_replay_fwd_noalloc: one copy per GPU, allocated when the library's code
+// object is loaded on that GPU and held until the process ends. In host code this name only
+// stands for the symbol; its device address comes from hipGetSymbolAddress (noalloc_scratch).
+static __device__ __align__(256) char scratch[AUGTREE_NOALLOC_SCRATCH_BYTES];
 
 namespace augtree {
 namespace {
@@ -658,6 +664,48 @@ augtree_status step_prefill_dq(const Shape& s, const void* q_p, const void* k_p,
   return AUGTREE_OK;
 }
 
+// Device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept; the only mutable state of the library.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+augtree_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(AUGTREE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(AUGTREE_ERR_UNSUPPORTED, "device %d: the scratch table holds %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(AUGTREE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return AUGTREE_OK;
+}
+
+// augtree_replay_fwd on validated shapes with a workspace of replay_fwd_ws(s).total bytes
+augtree_status replay_fwd_on(const Shape& s, const void* k_p, const void* v_p, const void* q_r, const void* k_r,
+                             const void* v_r, void* o_r, float* lse_r, void* ws, hipStream_t st) {
+  const ReplayFwdWs w = replay_fwd_ws(s);
+  float* o_parts[2] = {reinterpret_cast<float*>(at(ws, w.o_a)), reinterpret_cast<float*>(at(ws, w.o_b))};
+  float* l_parts[2] = {reinterpret_cast<float*>(at(ws, w.lse_a)), reinterpret_cast<float*>(at(ws, w.lse_b))};
+  CHECK(transpose_range(s, v_p, s.Hkv, 0, s.P, 64, at(ws, w.vpt), st));
+  CHECK(transpose_branches(s, v_r, s.Hkv, 64, at(ws, w.vrt), st));
+  // (1) every branch row against the whole, unmasked prompt K/V: partial state a
+  CHECK(step_replay_prompt_fwd(s, k_p, at(ws, w.vpt), q_r, 0, s.P, o_parts[0], l_parts[0], st));
+  // (2) every branch row against its own branch, causally: partial state b
+  CHECK(step_replay_local_fwd(s, q_r, k_r, at(ws, w.vrt), o_parts[1], l_parts[1], st));
+  // (3) log-sum-exp merge of a and b
+  const float* co[2] = {o_parts[0], o_parts[1]};
+  const float* cl[2] = {l_parts[0], l_parts[1]};
+  return step_merge(s, 2, co, cl, o_r, lse_r, st);
+}
+
 augtree_status check_key_range(const Shape& s, int kb, int ke) {
   if (kb < 0 || ke > s.P || kb >= ke)
     return fail(AUGTREE_ERR_INVALID_ARGUMENT, "prompt key range [%d, %d) not inside [0, %d) or empty", kb, ke, s.P);
@@ -878,21 +926,23 @@ augtree_status augtree_replay_fwd(const augtree_dims* dims, const void* k_p, con
   Shape s;
   CHECK(check_dims(dims, &s));
   PTR(k_p); PTR(v_p); PTR(q_r); PTR(k_r); PTR(v_r); PTR(o_r); PTR(lse_r);
-  const ReplayFwdWs w = replay_fwd_ws(s);
-  CHECK(check_ws(ws, ws_bytes, w.total));
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  float* o_parts[2] = {reinterpret_cast<float*>(at(ws, w.o_a)), reinterpret_cast<float*>(at(ws, w.o_b))};
-  float* l_parts[2] = {reinterpret_cast<float*>(at(ws, w.lse_a)), reinterpret_cast<float*>(at(ws, w.lse_b))};
-  CHECK(transpose_range(s, v_p, s.Hkv, 0, s.P, 64, at(ws, w.vpt), st));
-  CHECK(transpose_branches(s, v_r, s.Hkv, 64, at(ws, w.vrt), st));
-  // (1) every branch row against the whole, unmasked prompt K/V: partial state a
-  CHECK(step_replay_prompt_fwd(s, k_p, at(ws, w.vpt), q_r, 0, s.P, o_parts[0], l_parts[0], st));
-  // (2) every branch row against its own branch, causally: partial state b
-  CHECK(step_replay_local_fwd(s, q_r, k_r, at(ws, w.vrt), o_parts[1], l_parts[1], st));
-  // (3) log-sum-exp merge of a and b
-  const float* co[2] = {o_parts[0], o_parts[1]};
-  const float* cl[2] = {l_parts[0], l_parts[1]};
-  return step_merge(s, 2, co, cl, o_r, lse_r, st);
+  CHECK(check_ws(ws, ws_bytes, replay_fwd_ws(s).total));
+  return replay_fwd_on(s, k_p, v_p, q_r, k_r, v_r, o_r, lse_r, ws, static_cast<hipStream_t>(stream));
+}
+
+augtree_status augtree_replay_fwd_noalloc(const augtree_dims* dims, const void* k_p, const void* v_p,
+                                          const void* q_r, const void* k_r, const void* v_r, void* o_r,
+                                          float* lse_r, void* stream) {
+  Shape s;
+  CHECK(check_dims(dims, &s));
+  PTR(k_p); PTR(v_p); PTR(q_r); PTR(k_r); PTR(v_r); PTR(o_r); PTR(lse_r);
+  const size_t need = replay_fwd_ws(s).total;
+  if (need > (size_t)AUGTREE_NOALLOC_SCRATCH_BYTES)
+    return fail(AUGTREE_ERR_WORKSPACE, "this tree needs %zu bytes of scratch; the static scratch of the "
+                "no-allocation entry point holds %zu", need, (size_t)AUGTREE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  CHECK(noalloc_scratch(&ws));
+  return replay_fwd_on(s, k_p, v_p, q_r, k_r, v_r, o_r, lse_r, ws, static_cast<hipStream_t>(stream));
 }
 
 augtree_status augtree_replay_bwd(const augtree_dims* dims, const void* k_p, const void* v_p,

@@ -193,3 +193,14 @@ def test_prompt_bwd_rejects_a_workspace_smaller_than_its_range_needs():
         need = _lib.range_workspace_bytes(d, op, kb, ke)
         st = _lib.augtree_replay_prompt_bwd(d, *([FAKE] * 6), kb, ke, FAKE, FAKE, FAKE, need - 1, None)
         assert st == _lib.AUGTREE_ERR_WORKSPACE and "needed" in _lib.last_error()
+
+
+def test_noalloc_rejects_trees_beyond_its_scratch_before_any_call():
+    # the size check runs before the scratch lookup and before anything is enqueued
+    big, keep = _lib.make_dims(1024, [0, 100000], 32, 8, 128, 128 ** -0.5, _lib.AUGTREE_BF16)
+    assert _lib.workspace_bytes(big, _lib.AUGTREE_OP_REPLAY_FWD) > _lib.AUGTREE_NOALLOC_SCRATCH_BYTES
+    st = _lib.augtree_replay_fwd_noalloc(big, *([FAKE] * 7), None)
+    assert st == _lib.AUGTREE_ERR_WORKSPACE and "static scratch" in _lib.last_error()
+    d, keep2 = _dims()
+    st = _lib.augtree_replay_fwd_noalloc(d, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == _lib.AUGTREE_ERR_INVALID_ARGUMENT and "v_p is NULL" in _lib.last_error()
