@@ -184,7 +184,9 @@ class Runner:
                              "ranges of whole 256-key blocks")
         self.cuts = cuts
         shard_bufs = [(tr.empty(s.T, s.Hq, s.D, dtype=f32), tr.empty(s.Hq, s.T, dtype=f32)) for _ in range(nsh - 1)]
-        nws = max(_lib.workspace_bytes(tr.dims, op) for op in range(11))
+        nws = max(_lib.workspace_bytes(tr.dims, op) for op in range(13))
+        # shard layout: each shard's float32 dQ partial over its key range, plus the own-branch one
+        dq_parts = [tr.empty(s.T, s.Hq, s.D, dtype=f32) for _ in range(nsh + 1)] if nsh > 1 else []
         main = torch.cuda.current_stream(dev)
         self.nstreams = nstreams
         streams = [main] if nstreams == 1 else [torch.cuda.Stream(dev) for _ in range(3)]
@@ -207,8 +209,14 @@ class Runner:
             "replay_local_bwd": lambda ws: ops.replay_local_bwd(
                 tr, t["q_r"], t["k_r"], t["v_r"], b["lse_r"], b["rd_r"], t["do_r"], out=(b["dk_r"], b["dv_r"]),
                 ws=ws),
-            "replay_dq": lambda ws: ops.replay_dq(tr, t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], b["lse_r"],
-                                                  b["rd_r"], t["do_r"], out=b["dq_r"], ws=ws),
+            "replay_dq": (lambda ws: ops.replay_dq(tr, t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], b["lse_r"],
+                                                   b["rd_r"], t["do_r"], out=b["dq_r"], ws=ws)) if nsh == 1 else
+                         (lambda ws: ([ops.replay_prompt_dq(tr, t["k_p"], t["v_p"], t["q_r"], b["lse_r"], b["rd_r"],
+                                                            t["do_r"], cuts[i], cuts[i + 1], out=dq_parts[i], ws=ws)
+                                       for i in range(nsh)],
+                                      ops.replay_local_dq(tr, t["q_r"], t["k_r"], t["v_r"], b["lse_r"], b["rd_r"],
+                                                          t["do_r"], out=dq_parts[nsh], ws=ws),
+                                      ops.sum_parts(tr, dq_parts, out=b["dq_r"]))),
             "row_dot_p": lambda ws: ops.row_dot(tr, b["o_p"], t["do_p"], out=b["rd_p"]),
             "prefill_kv_bwd": lambda ws: ops.prefill_kv_bwd(
                 tr, t["q_p"], t["k_p"], t["v_p"], b["lse_p"], b["rd_p"], t["do_p"], b["dk_acc"], b["dv_acc"],
@@ -265,19 +273,31 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def stored_traffic(stage):
-    """HBM bytes per launch of ``stage`` from the committed counter runs, or None when they
-    were taken on other kernel sources or another workload."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def _stored(name, stage, workload):
+    """Record of ``stage`` in the committed counter summary profiles/<name>, or None when it was
+    taken on other kernel sources or another workload."""
+    path = os.path.join(ROOT, "profiles", name)
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     ent = rec.get("stages", {}).get(stage)
-    if ent is None or rec.get("kernel_sources_sha256") != kernel_source_digest():
+    if (ent is None or rec.get("kernel_sources_sha256") != kernel_source_digest()
+            or rec.get("workload") != workload):
         return None
     return ent
+
+
+def stored_traffic(stage, workload):
+    """HBM bytes per launch of ``stage`` (FETCH_SIZE + WRITE_SIZE counter runs, calibrated)."""
+    return _stored("traffic.json", stage, workload)
+
+
+def stored_mfma(stage, workload):
+    """Matrix-core counters of ``stage``'s kernels per launch: issued flops
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) and the busy fraction of the matrix cores."""
+    return _stored("mfma.json", stage, workload)
 
 
 def main() -> int:
@@ -297,8 +317,9 @@ def main() -> int:
                     help="skip timing the vendor bf16 GEMM reported beside the roofline peak")
     ap.add_argument("--kv-shards", type=int, default=1, choices=range(1, 8), metavar="{1..7}",
                     help="split the prompt K/V into this many stationary shards (the paper's MoveQ "
-                         "layout): the replay forward and the prompt K/V gradient run once per "
-                         "shard's key range and the merge combines shards + 1 partial states")
+                         "layout): the replay forward, the prompt K/V gradient and the branch dQ run "
+                         "once per shard's key range; the merge combines shards + 1 partial states and "
+                         "the dQ partials (shards + own branch) are summed in a fixed order")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run a plain elementwise copy of this many MiB "
                          "three times (a known-size kernel to scale HBM byte counters by)")
@@ -378,13 +399,26 @@ def main() -> int:
         if name in sb:
             entry["GB/s"] = round(sb[name] / (ms / 1e3) / 1e9, 1)
         kernels[name] = entry
+    wl = workload_name(cfg)
+    for name in sf:
+        mf = stored_mfma(name, wl) if nsh == 1 else None
+        if mf is not None:
+            # issued matrix work from the committed counter run of the same kernels and workload,
+            # over this run's time: makes the dQ passes' recompute visible
+            kernels[name]["issued_TFLOP/s"] = round(mf["issued_flops"] / (stage_ms[name] / 1e3) / 1e12, 1)
+            kernels[name]["mfma_busy"] = mf["busy"]
     dom = max(sf, key=lambda n: stage_ms[n])
     achieved = sf[dom] / (stage_ms[dom] / 1e3) / 1e12
-    tr_rec = stored_traffic(dom) if cfg == 4 and nsh == 1 else None
+    tr_rec = stored_traffic(dom, wl) if nsh == 1 else None
+    mf_rec = stored_mfma(dom, wl) if nsh == 1 else None
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": tr_rec["bytes_per_launch"] if tr_rec else None,
-                "alg_flops_per_launch": sf[dom], "avg_launch_ms": round(stage_ms[dom], 4)}
+                "alg_flops_per_launch": sf[dom], "avg_launch_ms": round(stage_ms[dom], 4),
+                "issued": (None if mf_rec is None else
+                           {"TFLOP/s": round(mf_rec["issued_flops"] / (stage_ms[dom] / 1e3) / 1e12, 1),
+                            "flops_per_launch": mf_rec["issued_flops"], "mfma_busy": mf_rec["busy"],
+                            "clock_GHz": mf_rec.get("clock_GHz"), "source": "profiles/mfma.json"})}
     if s.dtype == "bf16" and not args.no_gemm_reference:
         roofline["gemm_reference"] = gemm_reference(dev)
 

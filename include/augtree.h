@@ -79,7 +79,8 @@ enum { AUGTREE_OP_PREFILL_FWD = 0, AUGTREE_OP_REPLAY_FWD = 1, AUGTREE_OP_REPLAY_
        AUGTREE_OP_PREFILL_BWD = 3, AUGTREE_OP_REPLAY_PROMPT_BWD = 4,
        AUGTREE_OP_REPLAY_PROMPT_FWD = 5, AUGTREE_OP_REPLAY_LOCAL_FWD = 6,
        AUGTREE_OP_REPLAY_LOCAL_BWD = 7, AUGTREE_OP_REPLAY_DQ = 8, AUGTREE_OP_PREFILL_KV_BWD = 9,
-       AUGTREE_OP_PREFILL_DQ = 10 };
+       AUGTREE_OP_PREFILL_DQ = 10, AUGTREE_OP_REPLAY_PROMPT_DQ = 11,
+       AUGTREE_OP_REPLAY_LOCAL_DQ = 12 };
 
 /* Most partial states augtree_merge_partials accepts in one call. */
 #define AUGTREE_MAX_PARTS 8
@@ -176,6 +177,8 @@ augtree_status augtree_replay_fwd_noalloc(const augtree_dims *dims, const void *
  *   replay_fwd  = replay_prompt_fwd(0, P) + replay_local_fwd + merge_partials(2 parts)
  *   replay_bwd  = row_dot(T_R rows) + replay_prompt_bwd(0, P) + replay_local_bwd + replay_dq
  *   prefill_bwd = row_dot(P rows) + prefill_kv_bwd + prefill_dq
+ * and, in the prompt-K/V shard layout, replay_dq = sum_parts(replay_prompt_dq per shard range
+ * + replay_local_dq) up to float32 rounding.
  * A prompt key range [key_begin, key_end) lets one call act as one stationary prompt-K/V
  * shard of §3.3 MoveQ: the shard's partial states are later merged per query row.
  * Each step with a workspace takes the size of its own AUGTREE_OP_* code.
@@ -241,6 +244,32 @@ augtree_status augtree_replay_dq(const augtree_dims *dims, const void *k_p, cons
                                  const void *q_r, const void *k_r, const void *v_r,
                                  const float *lse_r, const float *rowdot_r, const void *do_r,
                                  void *dq_r, void *ws, size_t ws_bytes, void *stream);
+
+/* dQ of every branch row over prompt keys [key_begin, key_end) only, as float32 partial sums
+ * dq_part [T_R][Hq][D] (§3.3 MoveQ: a stationary prompt-K/V shard returns each query's gradient
+ * share to the query's owner through the reverse communication of its custom autograd
+ * operator). lse_r and rowdot_r are the rows' full statistics (over all their keys), so the
+ * shards' partials plus the own-branch partial add up to dQ; augtree_sum_parts adds them in
+ * a fixed order. 0 <= key_begin < key_end <= P. Workspace: augtree_range_workspace_bytes(dims,
+ * AUGTREE_OP_REPLAY_PROMPT_DQ, key_begin, key_end) (a transposed copy of the range's K). */
+augtree_status augtree_replay_prompt_dq(const augtree_dims *dims, const void *k_p, const void *v_p,
+                                        const void *q_r, const float *lse_r, const float *rowdot_r,
+                                        const void *do_r, int32_t key_begin, int32_t key_end,
+                                        float *dq_part, void *ws, size_t ws_bytes, void *stream);
+
+/* dQ of every branch row over its own branch keys only (causal, §3.2 Eq. 1), as float32
+ * partial sums dq_part [T_R][Hq][D]. Workspace: AUGTREE_OP_REPLAY_LOCAL_DQ (a transposed K_R). */
+augtree_status augtree_replay_local_dq(const augtree_dims *dims, const void *q_r, const void *k_r,
+                                       const void *v_r, const float *lse_r, const float *rowdot_r,
+                                       const void *do_r, float *dq_part, void *ws, size_t ws_bytes,
+                                       void *stream);
+
+/* out [rows][Hq][D] (dtype) = sum of num_parts (1..AUGTREE_MAX_PARTS) float32 partials of the
+ * same layout, added in index order and rounded once; rows = P or T_R. parts is a HOST array of
+ * device pointers. Used for the dQ partials of several prompt-K/V shards plus the own-branch
+ * partial. */
+augtree_status augtree_sum_parts(const augtree_dims *dims, int32_t rows, int32_t num_parts,
+                                 const float *const *parts, void *out, void *stream);
 
 /* Prompt dK/dV: the prompt queries' causal contribution plus dk_p_acc/dv_p_acc (or
  * nothing when both are NULL), rounded once: dk_p/dv_p [P][Hkv][D] (dtype).

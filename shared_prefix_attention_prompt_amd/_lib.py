@@ -30,6 +30,8 @@ AUGTREE_OP_REPLAY_LOCAL_BWD = 7
 AUGTREE_OP_REPLAY_DQ = 8
 AUGTREE_OP_PREFILL_KV_BWD = 9
 AUGTREE_OP_PREFILL_DQ = 10
+AUGTREE_OP_REPLAY_PROMPT_DQ = 11
+AUGTREE_OP_REPLAY_LOCAL_DQ = 12
 AUGTREE_MAX_BRANCHES = 128
 AUGTREE_MAX_PARTS = 8
 AUGTREE_ASSIGN_EXACT_MAX = 16
@@ -39,7 +41,8 @@ ENTRY_POINTS = ["augtree_prefill_fwd", "augtree_replay_fwd", "augtree_replay_bwd
                 "augtree_prefill_bwd", "augtree_replay_prompt_fwd", "augtree_replay_local_fwd",
                 "augtree_merge_partials", "augtree_row_dot", "augtree_replay_prompt_bwd",
                 "augtree_replay_local_bwd", "augtree_replay_dq", "augtree_prefill_kv_bwd",
-                "augtree_prefill_dq", "augtree_assign_units", "augtree_replay_fwd_noalloc",
+                "augtree_prefill_dq", "augtree_replay_prompt_dq", "augtree_replay_local_dq",
+                "augtree_sum_parts", "augtree_assign_units", "augtree_replay_fwd_noalloc",
                 "augtree_workspace_bytes",
                 "augtree_range_workspace_bytes",
                 "augtree_status_string", "augtree_last_error", "augtree_abi_version"]
@@ -90,8 +93,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.augtree_prefill_kv_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.augtree_prefill_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.augtree_assign_units.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+    lib.augtree_replay_prompt_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
+    lib.augtree_replay_local_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.augtree_sum_parts.argtypes = [P, i32, i32, fpp, vp, vp]
     lib.augtree_replay_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
-    for name in ENTRY_POINTS[:15]:
+    for name in ENTRY_POINTS[:18]:
         getattr(lib, name).restype = st
     lib.augtree_workspace_bytes.argtypes = [P, ctypes.c_int]
     lib.augtree_workspace_bytes.restype = sz
@@ -222,3 +228,20 @@ def augtree_prefill_kv_bwd(dims, q_p, k_p, v_p, lse_p, rowdot_p, do_p, dk_p_acc,
 def augtree_prefill_dq(dims, q_p, k_p, v_p, lse_p, rowdot_p, do_p, dq_p, ws, ws_bytes, stream) -> int:
     return load().augtree_prefill_dq(ctypes.byref(dims), q_p, k_p, v_p, lse_p, rowdot_p, do_p, dq_p, ws,
                                      ws_bytes, stream)
+
+
+def augtree_replay_prompt_dq(dims, k_p, v_p, q_r, lse_r, rowdot_r, do_r, key_begin, key_end, dq_part, ws,
+                             ws_bytes, stream) -> int:
+    return load().augtree_replay_prompt_dq(ctypes.byref(dims), k_p, v_p, q_r, lse_r, rowdot_r, do_r,
+                                           int(key_begin), int(key_end), dq_part, ws, ws_bytes, stream)
+
+
+def augtree_replay_local_dq(dims, q_r, k_r, v_r, lse_r, rowdot_r, do_r, dq_part, ws, ws_bytes, stream) -> int:
+    return load().augtree_replay_local_dq(ctypes.byref(dims), q_r, k_r, v_r, lse_r, rowdot_r, do_r, dq_part,
+                                          ws, ws_bytes, stream)
+
+
+def augtree_sum_parts(dims, rows, parts, out, stream) -> int:
+    n = len(parts)
+    arr = (ctypes.c_void_p * max(n, 1))(*parts)
+    return load().augtree_sum_parts(ctypes.byref(dims), int(rows), n, arr, out, stream)

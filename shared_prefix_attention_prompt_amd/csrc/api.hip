@@ -328,6 +328,8 @@ size_t op_workspace(const Shape& s, int op) {
     case AUGTREE_OP_REPLAY_DQ: return tr_prompt(s, s.Hkv) + tr_resp(s, s.Hkv);
     case AUGTREE_OP_PREFILL_KV_BWD: return 2 * tr_prompt(s, s.Hq) + st_prompt(s) + prefill_split_ws(s);
     case AUGTREE_OP_PREFILL_DQ: return tr_prompt(s, s.Hkv);
+    case AUGTREE_OP_REPLAY_PROMPT_DQ: return tr_prompt(s, s.Hkv);
+    case AUGTREE_OP_REPLAY_LOCAL_DQ: return tr_resp(s, s.Hkv);
   }
   return 0;
 }
@@ -336,7 +338,8 @@ size_t op_workspace(const Shape& s, int op) {
 size_t range_workspace(const Shape& s, int op, int kb, int ke) {
   const int nkeys = ke - kb;
   switch (op) {
-    case AUGTREE_OP_REPLAY_PROMPT_FWD: return tr_bytes(s, s.Hkv, pad64(nkeys));
+    case AUGTREE_OP_REPLAY_PROMPT_FWD:
+    case AUGTREE_OP_REPLAY_PROMPT_DQ: return tr_bytes(s, s.Hkv, pad64(nkeys));
     case AUGTREE_OP_REPLAY_PROMPT_BWD: {
       const int n = split_for_range(s, nkeys, prompt_split_cap(s));
       return 2 * tr_resp(s, s.Hq) + st_resp(s) + (n > 1 ? split_bytes(s, (int64_t)n * nkeys) : 0);
@@ -601,8 +604,56 @@ augtree_status step_replay_dq(const Shape& s, const void* k_p, const void* kpt, 
   q.bt = branch_table(s, 32 * 8 / heads_per_wg(s.Hq / s.Hkv));
   q.ntiles = total_tiles(q.bt);
   q.nwg = q.ntiles * heads_slots(s);
+  q.own = 1;
   q.scale = s.scale; q.scale_log2 = s.scale * kLog2e;
-  LAUNCH(launch_dq(s.dtype, s.D, kDqResponse, q, st), "branch dQ");
+  LAUNCH(launch_dq(s.dtype, s.D, kDqResponse, false, q, st), "branch dQ");
+  return AUGTREE_OK;
+}
+
+// float32 dQ partial of every branch row over prompt keys [kb, ke) only; kpt: transposed copy
+// of the range's K (pad64(ke - kb) columns)
+augtree_status step_replay_prompt_dq(const Shape& s, const void* k_p, const void* kpt, const void* v_p,
+                                     const void* q_r, const float* lse_r, const float* rowdot_r, const void* do_r,
+                                     int kb, int ke, float* dq_part, hipStream_t st) {
+  const size_t koff = (size_t)kb * s.Hkv * s.D * s.esz();
+  DqArgs q;
+  memset(&q, 0, sizeof(q));
+  q.q = q_r; q.dout = do_r; q.lse = lse_r; q.rowdot = rowdot_r;
+  q.kp = static_cast<const char*>(k_p) + koff;
+  q.vp = static_cast<const char*>(v_p) + koff;
+  q.kpt = kpt;
+  q.k = q.kp; q.v = q.vp; q.kt = kpt;  // own keys are not walked
+  q.dq = dq_part;
+  q.Hq = s.Hq; q.Hkv = s.Hkv;
+  q.nq_rows = s.T; q.nkv_rows = s.T; q.nprompt = ke - kb;
+  q.kt_cols = pad64(ke - kb); q.kpt_cols = pad64(ke - kb);
+  q.bt = branch_table(s, 32 * 8 / heads_per_wg(s.Hq / s.Hkv));
+  q.ntiles = total_tiles(q.bt);
+  q.nwg = q.ntiles * heads_slots(s);
+  q.own = 0;
+  q.scale = s.scale; q.scale_log2 = s.scale * kLog2e;
+  LAUNCH(launch_dq(s.dtype, s.D, kDqResponse, true, q, st), "branch dQ partial (prompt key range)");
+  return AUGTREE_OK;
+}
+
+// float32 dQ partial of every branch row over its own branch keys (causal)
+augtree_status step_replay_local_dq(const Shape& s, const void* q_r, const void* k_r, const void* krt,
+                                    const void* v_r, const float* lse_r, const float* rowdot_r, const void* do_r,
+                                    float* dq_part, hipStream_t st) {
+  DqArgs q;
+  memset(&q, 0, sizeof(q));
+  q.q = q_r; q.dout = do_r; q.lse = lse_r; q.rowdot = rowdot_r;
+  q.k = k_r; q.v = v_r; q.kt = krt; q.kp = k_r; q.vp = v_r; q.kpt = krt;  // no prompt keys walked
+  q.dq = dq_part;
+  q.Hq = s.Hq; q.Hkv = s.Hkv;
+  q.nq_rows = s.T; q.nkv_rows = s.T; q.nprompt = 0;
+  q.kt_cols = s.Tp(); q.kpt_cols = s.Tp();
+  q.bt = branch_table(s, 32 * 8 / heads_per_wg(s.Hq / s.Hkv));
+  q.ntiles = total_tiles(q.bt);
+  q.nwg = q.ntiles * heads_slots(s);
+  q.own = 1;
+  q.scale = s.scale; q.scale_log2 = s.scale * kLog2e;
+  LAUNCH(launch_dq(s.dtype, s.D, kDqResponse, true, q, st), "branch dQ partial (own branch keys)");
   return AUGTREE_OK;
 }
 
@@ -660,7 +711,7 @@ augtree_status step_prefill_dq(const Shape& s, const void* q_p, const void* k_p,
   q.ntiles = (s.P + rt - 1) / rt;
   q.nwg = q.ntiles * heads_slots(s);
   q.scale = s.scale; q.scale_log2 = s.scale * kLog2e;
-  LAUNCH(launch_dq(s.dtype, s.D, kDqPrefill, q, st), "prefill dQ");
+  LAUNCH(launch_dq(s.dtype, s.D, kDqPrefill, false, q, st), "prefill dQ");
   return AUGTREE_OK;
 }
 
@@ -869,6 +920,53 @@ augtree_status augtree_replay_dq(const augtree_dims* dims, const void* k_p, cons
   CHECK(transpose_range(s, k_p, s.Hkv, 0, s.P, 64, kpt, st));
   CHECK(transpose_branches(s, k_r, s.Hkv, 64, krt, st));
   return step_replay_dq(s, k_p, kpt, v_p, q_r, k_r, krt, v_r, lse_r, rowdot_r, do_r, dq_r, st);
+}
+
+augtree_status augtree_replay_prompt_dq(const augtree_dims* dims, const void* k_p, const void* v_p,
+                                        const void* q_r, const float* lse_r, const float* rowdot_r,
+                                        const void* do_r, int32_t key_begin, int32_t key_end, float* dq_part,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  CHECK(check_dims(dims, &s));
+  CHECK(check_key_range(s, key_begin, key_end));
+  PTR(k_p); PTR(v_p); PTR(q_r); PTR(lse_r); PTR(rowdot_r); PTR(do_r); PTR(dq_part);
+  CHECK(check_ws(ws, ws_bytes, range_workspace(s, AUGTREE_OP_REPLAY_PROMPT_DQ, key_begin, key_end)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  CHECK(transpose_range(s, k_p, s.Hkv, key_begin, key_end - key_begin, 64, ws, st));
+  return step_replay_prompt_dq(s, k_p, ws, v_p, q_r, lse_r, rowdot_r, do_r, key_begin, key_end, dq_part, st);
+}
+
+augtree_status augtree_replay_local_dq(const augtree_dims* dims, const void* q_r, const void* k_r, const void* v_r,
+                                       const float* lse_r, const float* rowdot_r, const void* do_r, float* dq_part,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  CHECK(check_dims(dims, &s));
+  PTR(q_r); PTR(k_r); PTR(v_r); PTR(lse_r); PTR(rowdot_r); PTR(do_r); PTR(dq_part);
+  CHECK(check_ws(ws, ws_bytes, op_workspace(s, AUGTREE_OP_REPLAY_LOCAL_DQ)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  CHECK(transpose_branches(s, k_r, s.Hkv, 64, ws, st));
+  return step_replay_local_dq(s, q_r, k_r, ws, v_r, lse_r, rowdot_r, do_r, dq_part, st);
+}
+
+augtree_status augtree_sum_parts(const augtree_dims* dims, int32_t rows, int32_t num_parts, const float* const* parts,
+                                 void* out, void* stream) {
+  Shape s;
+  CHECK(check_dims(dims, &s));
+  if (rows != s.P && rows != s.T)
+    return fail(AUGTREE_ERR_INVALID_ARGUMENT, "rows %d is neither P=%d nor T_R=%d", rows, s.P, s.T);
+  if (num_parts < 1 || num_parts > AUGTREE_MAX_PARTS)
+    return fail(AUGTREE_ERR_INVALID_ARGUMENT, "num_parts %d outside [1, %d]", num_parts, AUGTREE_MAX_PARTS);
+  if (parts == nullptr) return fail(AUGTREE_ERR_INVALID_ARGUMENT, "parts must be a host array");
+  for (int i = 0; i < num_parts; ++i) CHECK(check_ptr(parts[i], "parts[i]"));
+  PTR(out);
+  SumPartsArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int i = 0; i < num_parts; ++i) a.part[i] = parts[i];
+  a.nparts = num_parts;
+  a.out = out;
+  a.n = (int64_t)rows * s.Hq * s.D;
+  LAUNCH(launch_sum_parts(s.dtype, a, static_cast<hipStream_t>(stream)), "sum of partials");
+  return AUGTREE_OK;
 }
 
 augtree_status augtree_prefill_kv_bwd(const augtree_dims* dims, const void* q_p, const void* k_p,

@@ -18,7 +18,9 @@
 // one kv head, whose walks start at different rows, read the same rows at the same time.
 //
 // dQ is computed query-stationary in its own pass (it recomputes S and dP), which keeps it
-// free of atomics as well.
+// free of atomics as well. For one stationary prompt-K/V shard (a prompt key range) the pass
+// writes float32 partial sums over the range; the partials of the shards and of the rows' own
+// branch keys are then added in a fixed order (aux.hip, sum_parts_kernel).
 //
 // Query tiles (dK/dV) and key tiles (dQ) are copied global -> LDS by direct loads through a
 // ring of LDS stages, both in natural layout and from the transposed copies (the operands of
@@ -330,7 +332,7 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
     }
 }
 
-template <typename T, int D, int MODE, int HG>
+template <typename T, typename OT, int D, int MODE, int HG>
 __global__ __launch_bounds__(512, 2) void dq_kernel(DqArgs a) {
   using M = Mma<T>;
   constexpr int NW = 8;
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(512, 2) void dq_kernel(DqArgs a) {
     q1 = min(q0 + RT, be);
     n0 = (a.nprompt + BN - 1) / BN;
     kb0 = bs;
-    kb1 = q1;
+    kb1 = a.own ? q1 : bs;  // own branch keys, or none (a prompt key range alone)
     pcol0 = a.bt.pad[b];
   } else {
     tile = a.ntiles - 1 - tile;  // longest causal row range first
@@ -531,12 +533,12 @@ __global__ __launch_bounds__(512, 2) void dq_kernel(DqArgs a) {
   run_pipeline<NSTAGE, stage_copies<NW, TN, TN, TT>()>(nkt, issue, compute);
 
   if (!qvalid) return;
-  T* out = reinterpret_cast<T*>(a.dq) + (int64_t)qrow * qld + (int64_t)h * D;
+  OT* out = reinterpret_cast<OT*>(a.dq) + (int64_t)qrow * qld + (int64_t)h * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4)
-      store4<T>(out + db * 32 + r4 * 8 + g * 4, dqt[db][r4 * 4] * a.scale, dqt[db][r4 * 4 + 1] * a.scale,
+      store4<OT>(out + db * 32 + r4 * 8 + g * 4, dqt[db][r4 * 4] * a.scale, dqt[db][r4 * 4 + 1] * a.scale,
                 dqt[db][r4 * 4 + 2] * a.scale, dqt[db][r4 * 4 + 3] * a.scale);
 }
 
@@ -567,30 +569,36 @@ hipError_t launch_dkdv(int dtype, int D, int mode, const DkdvArgs& a, hipStream_
 }
 
 template <typename T, int D, int HG>
-static hipError_t launch_dq_hg(int mode, const DqArgs& a, hipStream_t s) {
+static hipError_t launch_dq_hg(int mode, bool f32_out, const DqArgs& a, hipStream_t s) {
   dim3 grid(a.nwg), block(512);
   switch (mode) {
-    case kDqResponse: hipLaunchKernelGGL((dq_kernel<T, D, kDqResponse, HG>), grid, block, 0, s, a); break;
-    case kDqPrefill: hipLaunchKernelGGL((dq_kernel<T, D, kDqPrefill, HG>), grid, block, 0, s, a); break;
+    case kDqResponse:
+      if (f32_out) hipLaunchKernelGGL((dq_kernel<T, float, D, kDqResponse, HG>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((dq_kernel<T, T, D, kDqResponse, HG>), grid, block, 0, s, a);
+      break;
+    case kDqPrefill:
+      if (f32_out) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((dq_kernel<T, T, D, kDqPrefill, HG>), grid, block, 0, s, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_dq_t(int mode, const DqArgs& a, hipStream_t s) {
+static hipError_t launch_dq_t(int mode, bool f32_out, const DqArgs& a, hipStream_t s) {
   switch (heads_per_wg(a.Hq / a.Hkv)) {
-    case 4: return launch_dq_hg<T, D, 4>(mode, a, s);
-    case 2: return launch_dq_hg<T, D, 2>(mode, a, s);
-    default: return launch_dq_hg<T, D, 1>(mode, a, s);
+    case 4: return launch_dq_hg<T, D, 4>(mode, f32_out, a, s);
+    case 2: return launch_dq_hg<T, D, 2>(mode, f32_out, a, s);
+    default: return launch_dq_hg<T, D, 1>(mode, f32_out, a, s);
   }
 }
 
-hipError_t launch_dq(int dtype, int D, int mode, const DqArgs& a, hipStream_t s) {
+hipError_t launch_dq(int dtype, int D, int mode, bool f32_out, const DqArgs& a, hipStream_t s) {
   if (a.nwg == 0) return hipSuccess;
-  if (dtype == 1 && D == 128) return launch_dq_t<bf16, 128>(mode, a, s);
-  if (dtype == 1 && D == 64) return launch_dq_t<bf16, 64>(mode, a, s);
-  if (dtype == 0 && D == 64) return launch_dq_t<float, 64>(mode, a, s);
+  if (dtype == 1 && D == 128) return launch_dq_t<bf16, 128>(mode, f32_out, a, s);
+  if (dtype == 1 && D == 64) return launch_dq_t<bf16, 64>(mode, f32_out, a, s);
+  if (dtype == 0 && D == 64) return launch_dq_t<float, 64>(mode, f32_out, a, s);
   return hipErrorInvalidValue;
 }
 

@@ -234,6 +234,28 @@ hipError_t launch_rowdot(int dtype, int D, const RowDotArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// Fixed-order sum of float32 partial sums (e.g. the dQ partials of several prompt-K/V shards
+// and of the rows' own branch keys), rounded once to the output type. Four elements per lane.
+template <typename T>
+__global__ __launch_bounds__(256) void sum_parts_kernel(SumPartsArgs a) {
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i4 >= a.n) return;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(a.part[0] + i4);
+  for (int p = 1; p < a.nparts; ++p) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(a.part[p] + i4);
+    acc[0] += x[0]; acc[1] += x[1]; acc[2] += x[2]; acc[3] += x[3];
+  }
+  store4<T>(reinterpret_cast<T*>(a.out) + i4, acc[0], acc[1], acc[2], acc[3]);
+}
+
+hipError_t launch_sum_parts(int dtype, const SumPartsArgs& a, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.n / 4 + 255) / 256));
+  if (dtype == 1) hipLaunchKernelGGL(sum_parts_kernel<bf16>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(sum_parts_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_split_reduce(const SplitReduceArgs& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
   const int64_t n4 = a.n / 4;

@@ -110,6 +110,7 @@ struct DqArgs {
   int32_t nq_rows, nkv_rows, nprompt, kt_cols, kpt_cols;
   int32_t ntiles;
   int32_t nwg;
+  int32_t own;        // response mode: 1 = also walk each row's own branch keys (causal)
   float scale, scale_log2;
   BranchTable bt;
 };
@@ -124,6 +125,13 @@ struct PrefillReduceArgs {
   int64_t n;               // P * Hkv * D
   int32_t row_elems;       // Hkv * D
   int32_t nz, zc;
+};
+
+struct SumPartsArgs {      // out[i] = sum_p part[p][i], p = 0..nparts-1 in order, rounded once
+  const float* part[kMaxParts];
+  int32_t nparts;
+  void* out;              // dtype
+  int64_t n;              // elements (a multiple of 4)
 };
 
 struct SplitReduceArgs {   // out[i] = sum_s part[s][i], s = 0..nsplit-1 in order
@@ -147,7 +155,9 @@ hipError_t launch_attn_fwd(int dtype, int D, int mode, const FwdArgs& a, hipStre
 hipError_t launch_merge(int dtype, int D, const MergeArgs& a, hipStream_t s);
 hipError_t launch_rowdot(int dtype, int D, const RowDotArgs& a, hipStream_t s);
 hipError_t launch_dkdv(int dtype, int D, int mode, const DkdvArgs& a, hipStream_t s);
-hipError_t launch_dq(int dtype, int D, int mode, const DqArgs& a, hipStream_t s);
+// f32_out: write float32 partial sums (response mode) instead of dtype
+hipError_t launch_dq(int dtype, int D, int mode, bool f32_out, const DqArgs& a, hipStream_t s);
+hipError_t launch_sum_parts(int dtype, const SumPartsArgs& a, hipStream_t s);
 hipError_t launch_split_reduce(const SplitReduceArgs& a, hipStream_t s);
 hipError_t launch_prefill_reduce(int dtype, const PrefillReduceArgs& a, hipStream_t s);
 

@@ -266,7 +266,7 @@ class Tree:
                 continue
             base = name.split("_")[0]
             rows = self.P if name.endswith("_p") or name.endswith("_p_acc") else self.T
-            if name in ("o_part",):
+            if name in ("o_part", "dq_part"):
                 _expect(name, t, (self.T, self.Hq, self.D), f32)
             elif name in ("lse_part",):
                 _expect(name, t, (self.Hq, self.T), f32)
@@ -408,6 +408,46 @@ def replay_dq(tr: Tree, k_p, v_p, q_r, k_r, v_r, lse_r, rowdot_r, do_r, out=None
                                 v_r.data_ptr(), lse_r.data_ptr(), rowdot_r.data_ptr(), do_r.data_ptr(),
                                 dq.data_ptr(), wp, wn, tr.stream())
     _lib._check(st, "augtree_replay_dq")
+    return dq
+
+
+def replay_prompt_dq(tr: Tree, k_p, v_p, q_r, lse_r, rowdot_r, do_r, key_begin: int = 0,
+                     key_end: Optional[int] = None, out=None, ws=None):
+    """float32 dQ partial [T][Hq][D] of every branch row over prompt keys [key_begin, key_end)
+    (one stationary prompt-K/V shard's share)."""
+    key_end = tr.P if key_end is None else key_end
+    _check_range(tr, key_begin, key_end)
+    dq = out if out is not None else tr.empty(tr.T, tr.Hq, tr.D, dtype=torch.float32)
+    tr.check(k_p=k_p, v_p=v_p, q_r=q_r, lse_r=lse_r, rowdot_r=rowdot_r, do_r=do_r, dq_part=dq)
+    wp, wn = tr.workspace(_lib.AUGTREE_OP_REPLAY_PROMPT_DQ, ws, (key_begin, key_end))
+    st = _lib.augtree_replay_prompt_dq(tr.dims, k_p.data_ptr(), v_p.data_ptr(), q_r.data_ptr(), lse_r.data_ptr(),
+                                       rowdot_r.data_ptr(), do_r.data_ptr(), key_begin, key_end, dq.data_ptr(),
+                                       wp, wn, tr.stream())
+    _lib._check(st, "augtree_replay_prompt_dq")
+    return dq
+
+
+def replay_local_dq(tr: Tree, q_r, k_r, v_r, lse_r, rowdot_r, do_r, out=None, ws=None):
+    """float32 dQ partial [T][Hq][D] of every branch row over its own branch keys."""
+    dq = out if out is not None else tr.empty(tr.T, tr.Hq, tr.D, dtype=torch.float32)
+    tr.check(q_r=q_r, k_r=k_r, v_r=v_r, lse_r=lse_r, rowdot_r=rowdot_r, do_r=do_r, dq_part=dq)
+    wp, wn = tr.workspace(_lib.AUGTREE_OP_REPLAY_LOCAL_DQ, ws)
+    st = _lib.augtree_replay_local_dq(tr.dims, q_r.data_ptr(), k_r.data_ptr(), v_r.data_ptr(), lse_r.data_ptr(),
+                                      rowdot_r.data_ptr(), do_r.data_ptr(), dq.data_ptr(), wp, wn, tr.stream())
+    _lib._check(st, "augtree_replay_local_dq")
+    return dq
+
+
+def sum_parts(tr: Tree, parts, out=None):
+    """dtype [rows][Hq][D] = fixed-order sum of float32 partials of that layout (rows = T_R)."""
+    if not 1 <= len(parts) <= _lib.AUGTREE_MAX_PARTS:
+        raise ValueError(f"{len(parts)} parts, 1..{_lib.AUGTREE_MAX_PARTS} allowed")
+    for p in parts:
+        tr.check(dq_part=p)
+    dq = out if out is not None else tr.empty(tr.T, tr.Hq, tr.D)
+    tr.check(dq_r=dq)
+    st = _lib.augtree_sum_parts(tr.dims, tr.T, [p.data_ptr() for p in parts], dq.data_ptr(), tr.stream())
+    _lib._check(st, "augtree_sum_parts")
     return dq
 
 

@@ -93,3 +93,31 @@ def test_merge_of_one_part_is_a_copy_and_empty_key_range_rejected():
     st = _lib.augtree_replay_prompt_fwd(tr.dims, t["k_p"].data_ptr(), t["v_p"].data_ptr(), t["q_r"].data_ptr(),
                                         10, 10, o.data_ptr(), l.data_ptr(), None, 0, None)
     assert st == _lib.AUGTREE_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("cuts", [[0, 517], [0, 100, 101, 300, 517], [0, 64, 128, 256, 384, 500, 510, 517],
+                                  [0, 1, 2, 3, 4, 5, 6, 517]])
+def test_moveq_sharded_dq_matches_oracle(cuts):
+    # dQ of the branch rows in the prompt-K/V shard layout: each shard's float32 partial over its
+    # key range (with the rows' full LSE and row dot), the own-branch partial, and their
+    # fixed-order sum, for 1..7 uneven shards
+    P = cuts[-1]
+    w = make_inputs(make_shape(P, [40, 129, 3], 8, 2, 128, dtype="bf16"), seed=10 + len(cuts))
+    s = w.shape
+    t = upload(w)
+    tr = ops.Tree(s.P, s.offsets, s.Hq, s.Hkv, s.D, s.torch_dtype, "cuda:0")
+    full = run_path(w, t)
+    rd_r = ops.row_dot(tr, full["o_r"], t["do_r"])
+    parts = [ops.replay_prompt_dq(tr, t["k_p"], t["v_p"], t["q_r"], full["lse_r"], rd_r, t["do_r"], a, b)
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    parts.append(ops.replay_local_dq(tr, t["q_r"], t["k_r"], t["v_r"], full["lse_r"], rd_r, t["do_r"]))
+    dq = ops.sum_parts(tr, parts)
+    torch.cuda.synchronize()
+    log(f"dQ shards {cuts}")
+    ref = flattened_tree_attention(w.q_p, w.k_p, w.v_p, w.q_r, w.k_r, w.v_r, w.offsets, do_p=w.do_p, do_r=w.do_r)
+    compare("dq_r (sharded)", dq, ref["dq_r"], "bf16")
+    # the same sums as the one-pass dQ up to float32 rounding of the partials
+    assert torch.allclose(dq.float(), full["dq_r"].float(), atol=1e-2, rtol=1e-2)
+    # each shard's partial alone is not the whole gradient (the shards really split the keys)
+    if len(parts) > 2:
+        assert not torch.allclose(parts[0], dq.float(), atol=1e-2)

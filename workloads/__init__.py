@@ -229,6 +229,16 @@ def make_chain_inputs(P: int, lens: Sequence[int], W: int, Hq: int, Hkv: int, D:
     return x_p, x_r, off, ws, rn(P, W), rn(T, W)
 
 
+def make_lm_head(W: int, vocab: int, G: int, seed: int, dtype: torch.dtype = torch.float64):
+    """A random language-model head and the first response token of every branch, drawn from
+    their own CPU generator: w_lm [W][vocab] (N(0, 1/W)) and first_tokens [G] (uniform token
+    ids in [0, vocab))."""
+    g = torch.Generator().manual_seed(int(seed))
+    w_lm = (torch.randn(W, vocab, generator=g, dtype=torch.float64) * W ** -0.5).to(dtype)
+    first = torch.randint(0, vocab, (G,), generator=g)
+    return w_lm, first
+
+
 # ---- work accounting (counts of (query, key) pairs; no attention arithmetic) ----
 
 def pairs_reuse(shape: Shape) -> int:
