@@ -282,11 +282,11 @@ def _stored(name, stage, workload):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = rec.get("stages", {}).get(stage)
-    if (ent is None or rec.get("kernel_sources_sha256") != kernel_source_digest()
-            or rec.get("workload") != workload):
+    if rec.get("kernel_sources_sha256") != kernel_source_digest():
         return None
-    return ent
+    if "workloads" in rec:   # several workloads in one record
+        return rec["workloads"].get(workload, {}).get("stages", {}).get(stage)
+    return rec.get("stages", {}).get(stage) if rec.get("workload") == workload else None
 
 
 def stored_traffic(stage, workload):
