@@ -262,6 +262,13 @@ int64_t prompt_split_cap_whole(const Shape& s) {
   return n > 1 ? (int64_t)n * s.P : 0;
 }
 
+// Query-tile walk table of the prompt K/V gradient over all branch rows: 16 bytes per 32-row tile.
+size_t walk_bytes(const Shape& s) {
+  int64_t t = 0;
+  for (int i = 0; i < s.G; ++i) t += (s.off[i + 1] - s.off[i] + kDkdvBM - 1) / kDkdvBM;
+  return align_up((size_t)t * 16);
+}
+
 // Layout of a workspace as consecutive 256-byte aligned pieces.
 struct Layout {
   size_t total = 0;
@@ -286,7 +293,7 @@ ReplayFwdWs replay_fwd_ws(const Shape& s) {
   return w;
 }
 
-struct ReplayBwdWs { size_t rowdot, qrt, dort, stats, kpt, krt, split, total; };
+struct ReplayBwdWs { size_t rowdot, qrt, dort, stats, kpt, krt, walk, split, total; };
 ReplayBwdWs replay_bwd_ws(const Shape& s) {
   ReplayBwdWs w;
   Layout l;
@@ -296,6 +303,7 @@ ReplayBwdWs replay_bwd_ws(const Shape& s) {
   w.stats = l.add(st_resp(s));
   w.kpt = l.add(tr_prompt(s, s.Hkv));
   w.krt = l.add(tr_resp(s, s.Hkv));
+  w.walk = l.add(walk_bytes(s));
   w.split = l.add(split_bytes(s, prompt_split_cap_whole(s)));
   w.total = l.total;
   return w;
@@ -321,7 +329,8 @@ size_t op_workspace(const Shape& s, int op) {
     case AUGTREE_OP_REPLAY_FWD: return replay_fwd_ws(s).total;
     case AUGTREE_OP_REPLAY_BWD: return replay_bwd_ws(s).total;
     case AUGTREE_OP_PREFILL_BWD: return prefill_bwd_ws(s).total;
-    case AUGTREE_OP_REPLAY_PROMPT_BWD: return 2 * tr_resp(s, s.Hq) + st_resp(s) + split_bytes(s, prompt_split_cap(s));
+    case AUGTREE_OP_REPLAY_PROMPT_BWD:
+      return 2 * tr_resp(s, s.Hq) + st_resp(s) + walk_bytes(s) + split_bytes(s, prompt_split_cap(s));
     case AUGTREE_OP_REPLAY_PROMPT_FWD: return tr_prompt(s, s.Hkv);
     case AUGTREE_OP_REPLAY_LOCAL_FWD: return tr_resp(s, s.Hkv);
     case AUGTREE_OP_REPLAY_LOCAL_BWD: return 2 * tr_resp(s, s.Hq) + st_resp(s);
@@ -342,7 +351,7 @@ size_t range_workspace(const Shape& s, int op, int kb, int ke) {
     case AUGTREE_OP_REPLAY_PROMPT_DQ: return tr_bytes(s, s.Hkv, pad64(nkeys));
     case AUGTREE_OP_REPLAY_PROMPT_BWD: {
       const int n = split_for_range(s, nkeys, prompt_split_cap(s));
-      return 2 * tr_resp(s, s.Hq) + st_resp(s) + (n > 1 ? split_bytes(s, (int64_t)n * nkeys) : 0);
+      return 2 * tr_resp(s, s.Hq) + st_resp(s) + walk_bytes(s) + (n > 1 ? split_bytes(s, (int64_t)n * nkeys) : 0);
     }
   }
   return op_workspace(s, op);
@@ -525,12 +534,12 @@ augtree_status step_row_dot(const Shape& s, int rows, const void* o, const void*
 }
 
 // qrt/dort: transposed branch copies of q_r / do_r; split: split-partial workspace
-// split: split-partial region of split_have bytes; cap_keys: the reserve the split count is
-// clamped to (parts x keys)
+// walk: walk-table region (walk_bytes); split: split-partial region of split_have bytes;
+// cap_keys: the reserve the split count is clamped to (parts x keys)
 augtree_status step_replay_prompt_bwd(const Shape& s, const void* k_p, const void* v_p, const void* q_r,
                                       const void* qrt, const float* stats, const void* do_r, const void* dort,
-                                      int kb, int ke, float* dk_acc, float* dv_acc, void* split, size_t split_have,
-                                      int64_t cap_keys, hipStream_t st) {
+                                      int kb, int ke, float* dk_acc, float* dv_acc, void* walk, void* split,
+                                      size_t split_have, int64_t cap_keys, hipStream_t st) {
   const int nkeys = ke - kb;
   const int nsplit = split_for_range(s, nkeys, cap_keys);
   if (nsplit > 1 && (size_t)2 * nsplit * nkeys * s.Hkv * s.D * sizeof(float) > split_have)
@@ -556,6 +565,14 @@ augtree_status step_replay_prompt_bwd(const Shape& s, const void* k_p, const voi
   p.bt = branch_table(s, kDkdvBM);
   p.nqtiles = total_tiles(p.bt);
   p.nwg = p.nktiles * s.Hkv * nsplit;
+  p.walk = static_cast<const int32_t*>(walk);
+  WalkTableArgs wt;
+  memset(&wt, 0, sizeof(wt));
+  wt.out = static_cast<int32_t*>(walk);
+  wt.ntiles = p.nqtiles;
+  wt.row_bytes = (int64_t)s.Hq * s.D * s.esz();
+  wt.bt = p.bt;
+  LAUNCH(launch_walk_table(wt, st), "walk table (prompt dK/dV)");
   p.scale = s.scale; p.scale_log2 = s.scale * kLog2e;
   LAUNCH(launch_dkdv(s.dtype, s.D, kDkdvPromptFromReplay, p, st), "prompt dK/dV from branches");
   if (nsplit > 1) {
@@ -880,13 +897,14 @@ augtree_status augtree_replay_prompt_bwd(const augtree_dims* dims, const void* k
   void* qrt = ws;
   void* dort = at(ws, tr_resp(s, s.Hq));
   float* stats = reinterpret_cast<float*>(at(ws, 2 * tr_resp(s, s.Hq)));
-  void* split = at(ws, 2 * tr_resp(s, s.Hq) + st_resp(s));
-  const size_t split_have = ws_bytes - (2 * tr_resp(s, s.Hq) + st_resp(s));
+  void* walk = at(ws, 2 * tr_resp(s, s.Hq) + st_resp(s));
+  void* split = at(ws, 2 * tr_resp(s, s.Hq) + st_resp(s) + walk_bytes(s));
+  const size_t split_have = ws_bytes - (2 * tr_resp(s, s.Hq) + st_resp(s) + walk_bytes(s));
   CHECK(transpose_branches(s, q_r, s.Hq, 32, qrt, st));
   CHECK(transpose_branches(s, do_r, s.Hq, 32, dort, st));
   CHECK(pack_stats_branches(s, lse_r, rowdot_r, stats, st));
   return step_replay_prompt_bwd(s, k_p, v_p, q_r, qrt, stats, do_r, dort, key_begin, key_end, dk_p_acc, dv_p_acc,
-                                split, split_have, prompt_split_cap(s), st);
+                                walk, split, split_have, prompt_split_cap(s), st);
 }
 
 augtree_status augtree_replay_local_bwd(const augtree_dims* dims, const void* q_r, const void* k_r,
@@ -1065,7 +1083,8 @@ augtree_status augtree_replay_bwd(const augtree_dims* dims, const void* k_p, con
   CHECK(pack_stats_branches(s, lse_r, rowdot, stats, st));
   // prompt keys x all branches' rows (no mask): the branch sum of the prompt gradient
   CHECK(step_replay_prompt_bwd(s, k_p, v_p, q_r, at(ws, w.qrt), stats, do_r, at(ws, w.dort), 0, s.P, dk_p_acc,
-                               dv_p_acc, at(ws, w.split), w.total - w.split, prompt_split_cap_whole(s), st));
+                               dv_p_acc, at(ws, w.walk), at(ws, w.split), w.total - w.split, prompt_split_cap_whole(s),
+                               st));
   // branch keys x own-branch rows (causal)
   CHECK(step_replay_local_bwd(s, q_r, at(ws, w.qrt), k_r, v_r, stats, do_r, at(ws, w.dort), dk_r, dv_r, st));
   // dQ of every branch row: prompt keys, then own-branch keys

@@ -143,22 +143,12 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
 
   // Query tiles are walked head by head (the group's query heads in turn), tiles t_lo ..
   // t_hi - 1 of each. The walk is a cursor advanced by one tile per issued stage (issue is
-  // called with consecutive iterations), so no iteration needs a division or a search of the
-  // branch table; the first row of each stage's tile is kept for the causal tests of compute.
-  struct Tile { int hq, row0, col0, nval; };
-  Tile cur{kvh * group, 0, 0, 0};
+  // called with consecutive iterations), so no iteration needs a division; over the branches'
+  // rows each tile's place comes from the per-launch walk table (one scalar load). The first
+  // row of each stage's tile is kept for the causal tests of compute.
+  struct Tile { int hq, row0, col0, nval; int64_t rowoff; };
+  Tile cur{kvh * group, 0, 0, 0, 0};
   int cur_it = -1, cur_t = t_lo - 1;
-  // mode 0: the branch of cur_t: its first tile, row offset, column offset, end row, and the
-  // first tile of the next branch
-  int b_first = 0, b_row = 0, b_col = 0, b_end = 0, b_next = 0, bb = 0;
-  auto enter_branch = [&](int nb) {
-    bb = nb;
-    b_first = a.bt.tile_prefix[nb];
-    b_row = a.bt.off[nb];
-    b_col = a.bt.pad[nb];
-    b_end = a.bt.off[nb + 1];
-    b_next = a.bt.tile_prefix[nb + 1];
-  };
   auto advance = [&]() {
     ++cur_it;
     bool restart = cur_it == 0;
@@ -168,12 +158,14 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
     }
     if (restart) cur_t = t_lo;
     if constexpr (MODE == kDkdvPromptFromReplay) {
-      if (restart) enter_branch(branch_of_tile(a.bt, cur_t));
-      else if (cur_t == b_next) enter_branch(bb + 1);
-      const int j = cur_t - b_first;
-      cur.row0 = b_row + j * BM;
-      cur.col0 = b_col + j * BM;
-      cur.nval = min(BM, b_end - cur.row0);
+      // one scalar load of the tile's entry in the walk table (the branch walk is done once
+      // per launch by walk_table_kernel, not by every wave at every stage)
+      typedef int i32x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(4))) const i32x4 const_i32x4;
+      const i32x4 e = ((const_i32x4*)a.walk)[cur_t];
+      cur.rowoff = (int64_t)(((uint64_t)(uint32_t)e[1] << 32) | (uint32_t)e[0]);
+      cur.col0 = e[2];
+      cur.nval = e[3];
     } else {
       // causal walks run from the last row tile down to the key block's own, so the
       // workgroups of one kv head (their key blocks start at different rows) walk the same
@@ -201,7 +193,9 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(DkdvArgs a) {
     if (cur_it < it) advance();
     const Tile& tl = cur;
     stage_row0[decltype(S)::value] = tl.row0;
-    const int64_t nat = ((int64_t)tl.row0 * a.Hq + tl.hq) * D * ESZ;
+    int64_t nat;
+    if constexpr (MODE == kDkdvPromptFromReplay) nat = tl.rowoff + (int64_t)tl.hq * (D * ESZ);
+    else nat = ((int64_t)tl.row0 * a.Hq + tl.hq) * D * ESZ;
     const int64_t tr = ((int64_t)tl.hq * a.qt_cols + tl.col0) * D * ESZ;  // tile-major copies
     plan.issue(stage(S), lane, TN{reinterpret_cast<const char*>(a.q) + nat, qld, tl.nval},
                   TN{reinterpret_cast<const char*>(a.dout) + nat, qld, tl.nval},
@@ -489,13 +483,15 @@ __global__ __launch_bounds__(512, 2) void dq_kernel(DqArgs a) {
       }
       // the mask test is taken once per tile, not per element, so that the unmasked
       // element loop is one straight block
+      // key kt + kb * 32 + crow(r, g) is masked beyond the last valid key and, for the rows'
+      // own keys, beyond the row: one per-lane limit against compile-time key offsets
+      const int lim = min(kend - 1, cz ? qrow : INT32_MAX) - kt - kb * 32 - 4 * g;
       auto softmax_grad = [&](auto masked) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], sl2, -lse2));
           if constexpr (decltype(masked)::value) {
-            const int kk = kt + kb * 32 + crow(r, g);
-            if (kk >= kend || (cz && kk > qrow)) p = 0.f;
+            if (crow(r, 0) > lim) p = 0.f;
           }
           pacc[r] = p * (pacc[r] - rdv);
         }

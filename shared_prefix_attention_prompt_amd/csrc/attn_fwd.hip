@@ -155,13 +155,14 @@ __global__ __launch_bounds__(kFwdWaves * 64, 2) void attn_fwd_kernel(FwdArgs a) 
     const char* lv = stage(S) + VOFF;
     const int kt = k0 + it * BN;
     if ((kt + BN > k1) || (causal && kt + BN - 1 > wq0)) {
+      // key kt + kb * 32 + crow(r, g) is masked beyond the last valid key and, causally, beyond
+      // the row: one per-lane limit per tile against compile-time key offsets
+      const int lim = min(k1 - 1, causal ? qrow : INT32_MAX) - kt - 4 * g;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt + kb * 32 + crow(r, g);
-          if (key >= k1 || (causal && key > qrow)) sacc[kb][r] = -kInf;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + crow(r, 0) > lim) sacc[kb][r] = -kInf;
     }
     // The next tile's scores go to the matrix cores (its stage has landed; past the last
     // tile it holds a repeat, whose scores are never used) interleaved, instruction by

@@ -256,6 +256,27 @@ hipError_t launch_sum_parts(int dtype, const SumPartsArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Query-tile table of the prompt K/V gradient walk (see WalkTableArgs): one thread per tile.
+__global__ __launch_bounds__(256) void walk_table_kernel(WalkTableArgs a) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.ntiles) return;
+  const int b = branch_of_tile(a.bt, t);
+  const int j = t - a.bt.tile_prefix[b];
+  const int row0 = a.bt.off[b] + j * kDkdvBM;
+  const int64_t off = (int64_t)row0 * a.row_bytes;
+  int32_t* e = a.out + 4 * (int64_t)t;
+  e[0] = (int32_t)(uint32_t)(uint64_t)off;
+  e[1] = (int32_t)((uint64_t)off >> 32);
+  e[2] = a.bt.pad[b] + j * kDkdvBM;
+  e[3] = min(kDkdvBM, a.bt.off[b + 1] - row0);
+}
+
+hipError_t launch_walk_table(const WalkTableArgs& a, hipStream_t s) {
+  if (a.ntiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(walk_table_kernel, dim3((unsigned)((a.ntiles + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_split_reduce(const SplitReduceArgs& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
   const int64_t n4 = a.n / 4;

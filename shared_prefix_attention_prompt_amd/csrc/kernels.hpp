@@ -90,9 +90,20 @@ struct DkdvArgs {
   int32_t causal;     // 1: a key only sees queries at or after it (branch and prefill walks)
   int32_t nwg;
   int64_t split_stride;  // elements between split partial buffers
+  const int32_t* walk;   // prompt-from-replay: per query tile {row byte offset lo, hi, column, rows}
   float scale, scale_log2;
   BranchTable bt;     // branches: offsets, padded offsets, tile prefix (query tiles for
                       // prompt-from-replay, key tiles for the branch walk)
+};
+
+// Table of the query tiles of every branch (32-row tiles, branches in order) for the walk of
+// the prompt K/V gradient over all branch rows: entry t = {low and high word of row0 * row_bytes,
+// column of the tile in the transposed copies, valid rows}. Written by walk_table_kernel.
+struct WalkTableArgs {
+  int32_t* out;        // [ntiles][4]
+  int32_t ntiles;
+  int64_t row_bytes;   // bytes between query rows (Hq * D * element size)
+  BranchTable bt;      // tile_prefix in 32-row tiles
 };
 
 enum DqMode { kDqResponse = 0, kDqPrefill = 1 };
@@ -159,6 +170,7 @@ hipError_t launch_dkdv(int dtype, int D, int mode, const DkdvArgs& a, hipStream_
 hipError_t launch_dq(int dtype, int D, int mode, bool f32_out, const DqArgs& a, hipStream_t s);
 hipError_t launch_sum_parts(int dtype, const SumPartsArgs& a, hipStream_t s);
 hipError_t launch_split_reduce(const SplitReduceArgs& a, hipStream_t s);
+hipError_t launch_walk_table(const WalkTableArgs& a, hipStream_t s);
 hipError_t launch_prefill_reduce(int dtype, const PrefillReduceArgs& a, hipStream_t s);
 
 constexpr int kDkdvKeysPerWG = 256;  // 8 waves x 32 keys
