@@ -1,4 +1,5 @@
-"""Builds libaugtree.so (the gfx950 HIP kernels + C ABI) in place, next to this file.
+"""Builds libaugtree.so (the gfx950 HIP kernels + C ABI) in place, next to this file, and the
+standalone issue-rate probe ``probe_rates`` (csrc/probe_rates.hip; not part of the library).
 
 Every source is compiled with hipcc for gfx950 only, in parallel, then linked into one
 shared library. Intermediate objects go to ``_build/`` beside the sources.
@@ -15,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libaugtree.so")
+PROBE = os.path.join(HERE, "probe_rates")
 SOURCES = ["api.hip", "attn_fwd.hip", "attn_bwd.hip", "aux.hip", "planner.hip"]
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -31,11 +33,23 @@ def _compile(src: str) -> str:
     return out
 
 
+def _probe() -> str:
+    tmp = PROBE + ".tmp"
+    cmd = [HIPCC, *FLAGS, os.path.join(CSRC, "probe_rates.hip"), "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for probe_rates.hip:\n{res.stderr}")
+    os.replace(tmp, PROBE)
+    return PROBE
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, (os.cpu_count() or 1)))
+    jobs = min(len(SOURCES) + 1, max(1, (os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
+        probe = ex.submit(_probe)
         objs = list(ex.map(_compile, SOURCES))
+        probe.result()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
