@@ -460,6 +460,7 @@ augtree_status pack_stats_branches(const Shape& s, const float* lse, const float
 // Single steps on validated shapes (no argument checks here). Transposed copies are passed
 // in, already written.
 // ---------------------------------------------------------------------------------------
+// head slots of the dQ kernel's grid (query heads / heads per workgroup)
 int heads_slots(const Shape& s) { return s.Hq / heads_per_wg(s.Hq / s.Hkv); }
 
 augtree_status step_prefill_fwd(const Shape& s, const void* q_p, const void* k_p, const void* vpt, void* o_p,
@@ -469,9 +470,9 @@ augtree_status step_prefill_fwd(const Shape& s, const void* q_p, const void* k_p
   a.q = q_p; a.k = k_p; a.vt = vpt; a.o = o_p; a.lse = lse_p;
   a.Hq = s.Hq; a.Hkv = s.Hkv;
   a.nq_rows = s.P; a.nkv_rows = s.P; a.vt_cols = pad64(s.P);
-  const int rt = fwd_rows_per_wg(s.Hq / s.Hkv);
+  const int rt = fwd_rows_per_wg(s.Hq / s.Hkv, kFwdPrefill);
   a.ntiles = (s.P + rt - 1) / rt;
-  a.nwg = a.ntiles * heads_slots(s);
+  a.nwg = a.ntiles * (s.Hq / fwd_heads_per_wg(s.Hq / s.Hkv, kFwdPrefill));
   a.scale_log2 = s.scale * kLog2e;
   LAUNCH(launch_attn_fwd(s.dtype, s.D, kFwdPrefill, a, st), "prefill forward");
   return AUGTREE_OK;
@@ -488,9 +489,9 @@ augtree_status step_replay_prompt_fwd(const Shape& s, const void* k_p, const voi
   a.o = o_part; a.lse = lse_part;
   a.Hq = s.Hq; a.Hkv = s.Hkv;
   a.nq_rows = s.T; a.nkv_rows = ke - kb; a.vt_cols = pad64(ke - kb);
-  const int rt = fwd_rows_per_wg(s.Hq / s.Hkv);
+  const int rt = fwd_rows_per_wg(s.Hq / s.Hkv, kFwdReplayPrompt);
   a.ntiles = (s.T + rt - 1) / rt;
-  a.nwg = a.ntiles * heads_slots(s);
+  a.nwg = a.ntiles * (s.Hq / fwd_heads_per_wg(s.Hq / s.Hkv, kFwdReplayPrompt));
   a.scale_log2 = s.scale * kLog2e;
   LAUNCH(launch_attn_fwd(s.dtype, s.D, kFwdReplayPrompt, a, st), "replay forward (prompt keys)");
   return AUGTREE_OK;
@@ -503,9 +504,9 @@ augtree_status step_replay_local_fwd(const Shape& s, const void* q_r, const void
   b.q = q_r; b.k = k_r; b.vt = vrt; b.o = o_part; b.lse = lse_part;
   b.Hq = s.Hq; b.Hkv = s.Hkv;
   b.nq_rows = s.T; b.nkv_rows = s.T; b.vt_cols = s.Tp();
-  b.bt = branch_table(s, fwd_rows_per_wg(s.Hq / s.Hkv));
+  b.bt = branch_table(s, fwd_rows_per_wg(s.Hq / s.Hkv, kFwdReplayLocal));
   b.ntiles = total_tiles(b.bt);
-  b.nwg = b.ntiles * heads_slots(s);
+  b.nwg = b.ntiles * (s.Hq / fwd_heads_per_wg(s.Hq / s.Hkv, kFwdReplayLocal));
   b.scale_log2 = s.scale * kLog2e;
   LAUNCH(launch_attn_fwd(s.dtype, s.D, kFwdReplayLocal, b, st), "replay forward (branch keys)");
   return AUGTREE_OK;
@@ -618,7 +619,7 @@ augtree_status step_replay_dq(const Shape& s, const void* k_p, const void* kpt, 
   q.Hq = s.Hq; q.Hkv = s.Hkv;
   q.nq_rows = s.T; q.nkv_rows = s.T; q.nprompt = s.P;
   q.kt_cols = s.Tp(); q.kpt_cols = pad64(s.P);
-  q.bt = branch_table(s, 32 * 8 / heads_per_wg(s.Hq / s.Hkv));
+  q.bt = branch_table(s, rows_per_wg(s.Hq / s.Hkv));
   q.ntiles = total_tiles(q.bt);
   q.nwg = q.ntiles * heads_slots(s);
   q.own = 1;
@@ -644,7 +645,7 @@ augtree_status step_replay_prompt_dq(const Shape& s, const void* k_p, const void
   q.Hq = s.Hq; q.Hkv = s.Hkv;
   q.nq_rows = s.T; q.nkv_rows = s.T; q.nprompt = ke - kb;
   q.kt_cols = pad64(ke - kb); q.kpt_cols = pad64(ke - kb);
-  q.bt = branch_table(s, 32 * 8 / heads_per_wg(s.Hq / s.Hkv));
+  q.bt = branch_table(s, rows_per_wg(s.Hq / s.Hkv));
   q.ntiles = total_tiles(q.bt);
   q.nwg = q.ntiles * heads_slots(s);
   q.own = 0;
@@ -665,7 +666,7 @@ augtree_status step_replay_local_dq(const Shape& s, const void* q_r, const void*
   q.Hq = s.Hq; q.Hkv = s.Hkv;
   q.nq_rows = s.T; q.nkv_rows = s.T; q.nprompt = 0;
   q.kt_cols = s.Tp(); q.kpt_cols = s.Tp();
-  q.bt = branch_table(s, 32 * 8 / heads_per_wg(s.Hq / s.Hkv));
+  q.bt = branch_table(s, rows_per_wg(s.Hq / s.Hkv));
   q.ntiles = total_tiles(q.bt);
   q.nwg = q.ntiles * heads_slots(s);
   q.own = 1;
@@ -724,7 +725,7 @@ augtree_status step_prefill_dq(const Shape& s, const void* q_p, const void* k_p,
   q.Hq = s.Hq; q.Hkv = s.Hkv;
   q.nq_rows = s.P; q.nkv_rows = s.P; q.nprompt = 0;
   q.kt_cols = pad64(s.P);
-  const int rt = 32 * 8 / heads_per_wg(s.Hq / s.Hkv);
+  const int rt = rows_per_wg(s.Hq / s.Hkv);
   q.ntiles = (s.P + rt - 1) / rt;
   q.nwg = q.ntiles * heads_slots(s);
   q.scale = s.scale; q.scale_log2 = s.scale * kLog2e;

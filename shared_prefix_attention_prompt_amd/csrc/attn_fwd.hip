@@ -8,7 +8,7 @@
 //
 // A workgroup is 8 waves of 32 query rows (two per SIMD); its waves cover HG query heads of
 // one key/value group (HG = 4 for grouped-query heads, so one staged K/V tile serves four
-// heads). K/V tiles of 64 keys go global -> LDS by direct loads through a 4-stage ring: while
+// heads; HG = 7 for seven heads per kv head in the branch-local mode, one wave idle). K/V tiles of 64 keys go global -> LDS by direct loads through a 4-stage ring: while
 // tile i is used, tile i + 1 is resident too (its scores are computed one iteration early,
 // interleaved with tile i's softmax) and two more are in flight.
 //
@@ -147,11 +147,10 @@ __global__ __launch_bounds__(kFwdWaves * 64, 2) void attn_fwd_kernel(FwdArgs a) 
     static_assert(NSTAGE % 2 == 0, "buffer parity follows the stage");
     f32x16 (&sacc)[KB] = sbuf[st & 1];
     f32x16 (&snext)[KB] = sbuf[nst & 1];
+    // a wave is active on a prefix of the tiles (the causal limit only grows), so an inactive
+    // wave needs no further scores
+    if (!active(it)) return;
     if (it == 0) scores(S, sacc);
-    if (!active(it)) {
-      scores(std::integral_constant<int, nst>{}, snext);
-      return;
-    }
     const char* lv = stage(S) + VOFF;
     const int kt = k0 + it * BN;
     if ((kt + BN > k1) || (causal && kt + BN - 1 > wq0)) {
@@ -266,7 +265,18 @@ __global__ __launch_bounds__(kFwdWaves * 64, 2) void attn_fwd_kernel(FwdArgs a) 
 }
 
 int heads_per_wg(int group) { return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1); }
-int fwd_rows_per_wg(int group) { return 32 * (kFwdWaves / heads_per_wg(group)); }
+int rows_per_wg(int group) { return 32 * (kFwdWaves / heads_per_wg(group)); }
+
+// Seven query heads per kv head (a prime group): the branch-local forward takes one 32-row
+// block of all seven heads per workgroup, the eighth wave idle, so that every wave walks the
+// same short causal key range (one head over eight row blocks leaves the waves near the
+// diagonal waiting at the stage barriers). The long walks keep one head per workgroup: there
+// the lone wave of the idle wave's SIMD, with no second wave to overlap its softmax with the
+// products, would set the pace at every barrier.
+int fwd_heads_per_wg(int group, int mode) {
+  return group == 7 && mode == kFwdReplayLocal ? 7 : heads_per_wg(group);
+}
+int fwd_rows_per_wg(int group, int mode) { return 32 * (kFwdWaves / fwd_heads_per_wg(group, mode)); }
 
 template <typename T, int D, int HG>
 static hipError_t launch_fwd_hg(int mode, const FwdArgs& a, hipStream_t s) {
@@ -282,9 +292,12 @@ static hipError_t launch_fwd_hg(int mode, const FwdArgs& a, hipStream_t s) {
 
 template <typename T, int D>
 static hipError_t launch_fwd_t(int mode, const FwdArgs& a, hipStream_t s) {
-  switch (heads_per_wg(a.Hq / a.Hkv)) {
+  switch (fwd_heads_per_wg(a.Hq / a.Hkv, mode)) {
     case 4: return launch_fwd_hg<T, D, 4>(mode, a, s);
     case 2: return launch_fwd_hg<T, D, 2>(mode, a, s);
+    case 7:
+      hipLaunchKernelGGL((attn_fwd_kernel<T, float, D, kFwdReplayLocal, 7>), dim3(a.nwg), dim3(kFwdWaves * 64), 0, s, a);
+      return hipGetLastError();
     default: return launch_fwd_hg<T, D, 1>(mode, a, s);
   }
 }

@@ -153,9 +153,12 @@ struct SplitReduceArgs {   // out[i] = sum_s part[s][i], s = 0..nsplit-1 in orde
 };
 
 // Heads per workgroup of the query-stationary kernels (the waves of a workgroup cover that
-// many query heads of one kv group) and query rows per forward workgroup.
+// many query heads of one kv group) and query rows per workgroup (8 waves of 32 rows over those
+// heads): the dQ kernel, and the forward kernel per mode (FwdMode).
 int heads_per_wg(int group);
-int fwd_rows_per_wg(int group);
+int rows_per_wg(int group);
+int fwd_heads_per_wg(int group, int mode);
+int fwd_rows_per_wg(int group, int mode);
 
 // Records `msg` as the calling thread's last error (augtree_last_error) and returns st.
 augtree_status set_error(augtree_status st, const char* msg);

@@ -70,6 +70,10 @@ def test_config1_fp32_full():
     (3000, [700, 45, 1210], 8, 2, 128, "bf16"),
     # the most branches a tree may have (128), short and uneven
     (33, [1 + (7 * i) % 23 for i in range(128)], 4, 2, 64, "bf16"),
+    # seven query heads per kv head: a workgroup takes one 32-row block of all seven heads
+    (300, [129, 40, 7], 7, 1, 128, "bf16"),
+    (130, [65, 1, 33], 14, 2, 64, "bf16"),
+    (90, [50, 3], 7, 1, 64, "f32"),
 ])
 def test_small_trees(P, lens, Hq, Hkv, D, dtype):
     w = make_inputs(make_shape(P, lens, Hq, Hkv, D, dtype=dtype, std=1.0 if dtype == "f32" else 0.5),
