@@ -74,6 +74,11 @@ def test_config1_fp32_full():
     (300, [129, 40, 7], 7, 1, 128, "bf16"),
     (130, [65, 1, 33], 14, 2, 64, "bf16"),
     (90, [50, 3], 7, 1, 64, "f32"),
+    # 3, 5 and 6 query heads per kv head (one or two heads per workgroup, groups that are not
+    # powers of two)
+    (200, [77, 30, 2], 6, 2, 128, "bf16"),
+    (150, [64, 9], 6, 1, 64, "bf16"),
+    (120, [40, 33], 5, 1, 64, "f32"),
 ])
 def test_small_trees(P, lens, Hq, Hkv, D, dtype):
     w = make_inputs(make_shape(P, lens, Hq, Hkv, D, dtype=dtype, std=1.0 if dtype == "f32" else 0.5),
