@@ -60,3 +60,35 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_stored_counters_only_for_their_sources_and_workload(monkeypatch):
+    # the committed counter records carry the digest of the kernel sources they were taken on:
+    # the bench reports them for that workload only, and not at all once a source changes
+    from workloads import workload_name
+    wl = workload_name(4)
+    tr = bench.stored_traffic("replay_prompt_bwd", wl)
+    mf = bench.stored_mfma("replay_prompt_bwd", wl)
+    assert tr is not None and tr["bytes_per_launch"] > 0
+    assert mf is not None and mf["issued_flops"] >= mf["algorithmic_flops"] > 0
+    assert 0.0 < mf["busy"] <= 1.0
+    assert bench.stored_traffic("replay_prompt_bwd", workload_name(5)) is None
+    assert bench.stored_mfma("replay_prompt_bwd", "no such workload") is None
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: "0" * 64)
+    assert bench.stored_traffic("replay_prompt_bwd", wl) is None
+    assert bench.stored_mfma("replay_prompt_bwd", wl) is None
+
+
+def test_stored_counter_records_match_their_summaries():
+    # every figure in the JSON records appears in the committed markdown summary it names, so
+    # the bench line and the readable summaries cannot drift apart
+    import json
+    rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+    for stage, r in rec["stages"].items():
+        md = open(os.path.join(ROOT, "profiles", r["summary"])).read()
+        assert f"| {r['fetch_kib']:.0f} | {r['write_kib']:.0f} | {r['bytes_per_launch'] / 1e9:.3f} |" in md, stage
+    mf = json.load(open(os.path.join(ROOT, "profiles", "mfma.json")))
+    for wl, w in mf["workloads"].items():
+        md = open(os.path.join(ROOT, "profiles", f"mfma_{wl}.md")).read()
+        for stage, r in w["stages"].items():
+            assert f"| {r['counter_ms']:.3f} | {r['issued_flops'] / 1e12:.3f} | {r['algorithmic_flops'] / 1e12:.3f} |" in md, (wl, stage)
